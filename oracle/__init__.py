@@ -1,0 +1,29 @@
+"""CPU oracle for the fully-FP4 (MXFP4 / NVFP4) quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, tables or
+constants with the HIP library; both are fed the same seeded inputs.
+
+It is a plain, slow, written-out restatement of what the pages compute:
+
+* "Quartet: Native FP4 Training Can Be Optimal for Large Language Models"
+  (the block Hadamard transform, MXFP4 quantization with RTN forward / SR
+  backward and the 3/4 and 16/9 rescales, the three FP4 GEMMs);
+* "Quartet II: Accurate LLM Pre-Training in NVFP4 by Improved Unbiased
+  Gradient Estimation" (the NVFP4 format, Four-over-Six, inner-dimension RHT);
+* "Bridging the Gap Between Promise and Performance for Microscaling FP4
+  Quantization" (the E2M1 / E8M0 / E4M3 formats, block Hadamard rotation).
+
+Every function names the passage it follows.  Where the pages leave a step
+open the reading taken is stated in the function's docstring.
+
+Pinned: codecs (exhaustive / library routes), the FWHT (Sylvester matrix,
+orthogonality), the RNG (published test vectors), SR (exact probabilities,
+unbiasedness), GEMM (brute-force triple loop), linear backward (expectation
+equals the exact gradient), NVFP4 RTN and RTN+4/6 (the pages' Table 1 MSEs).
+Parity unpinned: the FP8 staging of the NVFP4 GEMM (a design of this library
+that the pages do not describe; only its self-consistency is checked).
+"""
+
+from . import formats, rng, rht, mx, nvfp4  # noqa: F401

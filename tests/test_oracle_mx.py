@@ -1,0 +1,193 @@
+"""Pins for the oracle's MXFP4 quantizer, GEMM and linear layer."""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from oracle import formats, mx, rht, rng
+
+
+def _bf16ish(rs, shape, scale=1.0):
+    from fp4_microscaled_quantized_amd import synth
+    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits((rs.standard_normal(shape) * scale).astype(np.float32)))
+
+
+def _brute_block_rtn(x_block, mask, hadamard, rounding, u=None):
+    """Pure-Python restatement for one 32-block (integer-valued inputs make the
+    transform exact, so a plain matrix product stands in for the FWHT)."""
+    H = scipy.linalg.hadamard(32)
+    s = [(-1.0 if (mask >> j) & 1 else 1.0) for j in range(32)]
+    if hadamard:
+        t = [sum(H[i][j] * s[j] * float(x_block[j]) for j in range(32)) for i in range(32)]
+        y = [float(np.float32(np.float32(ti) * rht.INV_SQRT_G)) for ti in t]
+    else:
+        y = [float(v) for v in x_block]
+    amax = max(abs(v) for v in y)
+    e = 0 if amax == 0 else max(0, min(254, math.frexp(amax)[1] - 1 - 2 + 127))
+    out = []
+    for i, yi in enumerate(y):
+        if rounding == mx.RTN:
+            v = float(np.float32(np.float32(yi) * np.float32(2.0 ** (127 - e))))
+            best, bc = None, None
+            for c, g in enumerate(formats.E2M1_GRID):
+                d = abs(abs(v) - g)
+                if best is None or d < best or (d == best and c % 2 == 0):
+                    best, bc = d, c
+        else:
+            f = np.float32(0.75) * np.float32(2.0 ** (127 - e))
+            v = float(np.float32(np.float32(yi) * np.float32(f)))
+            grid = list(formats.E2M1_GRID)
+            lo = max(c for c, g in enumerate(grid) if g <= abs(v))
+            if lo == 7:
+                bc = 7
+            else:
+                p = (abs(v) - grid[lo]) / (grid[lo + 1] - grid[lo])
+                bc = lo + 1 if u[i] < p else lo
+        # a transformed value that is exactly zero may carry either sign (the
+        # fp32 butterflies keep IEEE signed zeros); mark it with None
+        out.append(None if yi == 0 else bc | (8 if math.copysign(1.0, v) < 0 else 0))
+    return out, e
+
+
+@pytest.mark.parametrize("rounding", [mx.RTN, mx.SR])
+@pytest.mark.parametrize("hadamard", [True, False])
+def test_quantize_vs_pure_python(rounding, hadamard):
+    rs = np.random.default_rng(11)
+    x = rs.integers(-40, 40, (3, 64)).astype(np.float32)
+    x[1] *= 1 / 64.0          # a small-magnitude row
+    x[2, :32] = 0.0           # an all-zero group
+    mask, seed, stream = 0x1234ABCD, 9, 3
+    codes, scales = mx.quantize(x, rounding=rounding, hadamard=hadamard, sign_mask=mask,
+                                seed=seed, stream=stream)
+    q = mx.unpack(codes)
+    for r in range(3):
+        for b in range(2):
+            idx = np.arange(r * 64 + b * 32, r * 64 + b * 32 + 32, dtype=np.uint64)
+            u = rng.uniform24(rng.bits(seed, stream, idx))
+            want, e = _brute_block_rtn(x[r, b * 32:(b + 1) * 32], mask, hadamard, rounding, u)
+            assert scales[r, b] == e
+            got = list(q[r, b * 32:(b + 1) * 32])
+            assert [g if w is not None else (g & 7) for g, w in zip(got, want)] == \
+                [w if w is not None else 0 for w in want]
+
+
+def test_col_axis_is_row_axis_of_transpose():
+    rs = np.random.default_rng(4)
+    x = _bf16ish(rs, (64, 96))
+    for rounding in (mx.RTN, mx.SR):
+        a = mx.quantize(x, rounding=rounding, axis=mx.COL, sign_mask=77, seed=1, stream=2)
+        b = mx.quantize(np.ascontiguousarray(x.T), rounding=rounding, axis=mx.ROW, sign_mask=77,
+                        seed=1, stream=2)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        assert a[0].shape == (96, 32) and a[1].shape == (96, 2)
+
+
+def test_scale_invariants_and_error_bounds():
+    rs = np.random.default_rng(5)
+    x = _bf16ish(rs, (32, 1024)) * np.float32(3.0)
+    y = rht.rht32(x, 0x55AA).astype(np.float64)
+    for rounding in (mx.RTN, mx.SR):
+        codes, scales = mx.quantize(x, rounding=rounding, sign_mask=0x55AA, seed=0, stream=1)
+        X = np.repeat(formats.e8m0_value(scales), 32, axis=1)
+        deq = mx.dequantize(codes, scales)
+        if rounding == mx.RTN:
+            # |error| <= X (half the top gap 2X); saturated (6X, 8X) values lose < 2X
+            assert np.all(np.abs(deq - y) <= 2 * X)
+            inside = np.abs(y) <= 6 * X
+            assert np.all((np.abs(deq - y) <= X)[inside])
+        else:
+            v = 0.75 * y / X
+            assert np.all(np.abs(v) < 6)
+            # SR picks one of the two bracketing grid points
+            assert np.all(np.abs(deq - 0.75 * y) <= 2 * X)
+
+
+def test_non_finite_group():
+    x = np.ones((2, 64), dtype=np.float32)
+    x[0, 5] = np.nan
+    x[1, 40] = np.inf
+    for had in (True, False):
+        c, s = mx.quantize(x, rounding=mx.RTN, hadamard=had)
+        assert s[0, 0] == 255 and s[1, 1] == 255
+        assert s[0, 1] != 255 and s[1, 0] != 255
+        q = mx.unpack(c)
+        assert np.all(q[0, :32] == 0) and np.all(q[1, 32:] == 0)
+
+
+def test_sr_quantizer_unbiased_over_seeds():
+    rs = np.random.default_rng(6)
+    x = _bf16ish(rs, (4, 64))
+    y = rht.rht32(x, 3).astype(np.float64)
+    n = 3000
+    acc = np.zeros_like(y)
+    acc2 = np.zeros_like(y)
+    for seed in range(n):
+        d = mx.dequantize(*mx.quantize(x, rounding=mx.SR, sign_mask=3, seed=seed, stream=1)) / 0.75
+        acc += d
+        acc2 += d * d
+    mean = acc / n
+    sd = np.sqrt(np.maximum(acc2 / n - mean ** 2, 0) / n) + 1e-12
+    assert np.all(np.abs(mean - y) < 5 * sd + 1e-9)
+
+
+def test_sr_mse_exceeds_rtn_mse():
+    # Quartet Table 2 / Quartet II Table 1 ranking: SR error > RTN error on Gaussian data
+    rs = np.random.default_rng(7)
+    x = rs.standard_normal((64, 4096)).astype(np.float32)
+    e = {}
+    for r in (mx.RTN, mx.SR):
+        d = mx.dequantize(*mx.quantize(x, rounding=r, hadamard=False, seed=1, stream=1))
+        d = d / (0.75 if r == mx.SR else 1.0)
+        e[r] = np.mean((d - x) ** 2)
+    assert e[mx.SR] > 1.5 * e[mx.RTN]
+
+
+def test_gemm_vs_triple_loop():
+    rs = np.random.default_rng(8)
+    a = mx.quantize(_bf16ish(rs, (3, 64)), rounding=mx.RTN, sign_mask=1)
+    b = mx.quantize(_bf16ish(rs, (5, 64)), rounding=mx.SR, sign_mask=1, seed=2, stream=1)
+    qa, qb = mx.unpack(a[0]), mx.unpack(b[0])
+    C = mx.gemm(*a, *b, alpha=16 / 9)
+    for i in range(3):
+        for j in range(5):
+            s = 0.0
+            for k in range(64):
+                va = float(formats.E2M1_GRID[qa[i, k] & 7]) * (-1 if qa[i, k] & 8 else 1)
+                vb = float(formats.E2M1_GRID[qb[j, k] & 7]) * (-1 if qb[j, k] & 8 else 1)
+                s += va * 2.0 ** (int(a[1][i, k // 32]) - 127) * vb * 2.0 ** (int(b[1][j, k // 32]) - 127)
+            assert abs(C[i, j] - 16 / 9 * s) <= 1e-12 * max(1.0, abs(s))
+
+
+def test_linear_forward_close_to_exact():
+    rs = np.random.default_rng(9)
+    x, w = _bf16ish(rs, (64, 128)), _bf16ish(rs, (96, 128), 0.02)
+    y, ctx = mx.linear_fwd(x, w, seed=3)
+    ref = x.astype(np.float64) @ w.T.astype(np.float64)
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert rel < 0.2
+    assert ctx["xt"][0].shape == (128, 32) and ctx["wt"][0].shape == (128, 48)
+
+
+def test_linear_backward_unbiased_1_over_B():
+    # Quartet II Appendix A "1/B" test: the error of the mean of B independent
+    # backward estimates falls like 1/B for an unbiased estimator.
+    rs = np.random.default_rng(10)
+    M, N, K = 64, 64, 64
+    x, w, dy = _bf16ish(rs, (M, K)), _bf16ish(rs, (N, K)), _bf16ish(rs, (M, N))
+    ex_dx = dy.astype(np.float64) @ w.astype(np.float64)
+    ex_dw = dy.T.astype(np.float64) @ x.astype(np.float64)
+    sums_dx, sums_dw = [], []
+    for seed in range(256):
+        _, ctx = mx.linear_fwd(x, w, seed)
+        dx, dw = mx.linear_bwd(dy, ctx)
+        sums_dx.append(dx)
+        sums_dw.append(dw)
+    sums_dx, sums_dw = np.array(sums_dx), np.array(sums_dw)
+
+    def mse(ests, ex, B):
+        m = ests[: (len(ests) // B) * B].reshape(-1, B, *ex.shape).mean(axis=1)
+        return np.mean((m - ex) ** 2)
+    for ests, ex in ((sums_dx, ex_dx), (sums_dw, ex_dw)):
+        e1, e16, e64 = mse(ests, ex, 1), mse(ests, ex, 16), mse(ests, ex, 64)
+        assert e16 < e1 / 8 and e64 < e1 / 30
