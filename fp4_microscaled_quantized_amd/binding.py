@@ -1,0 +1,272 @@
+"""Thin ctypes binding over libfp4mx.so (argument marshalling only).
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  Loading fails loudly when the
+library has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4mx.so")
+
+RTN, SR = 0, 1
+ROW, COL = 0, 1
+
+_lib = None
+
+_P = C.c_void_p
+_I64 = C.c_int64
+_U32 = C.c_uint32
+_U64 = C.c_uint64
+_INT = C.c_int
+_SZ = C.c_size_t
+
+
+class CtxStruct(C.Structure):
+    _fields_ = [("xt_codes", _P), ("xt_scales", _P), ("wt_codes", _P), ("wt_scales", _P),
+                ("seed", _U64)]
+
+
+_SIGS = {
+    "fp4mx_status_string": (C.c_char_p, [_INT]),
+    "fp4mx_last_hip_error": (_INT, []),
+    "fp4mx_sign_mask": (_U32, [_U64, _U32]),
+    "fp4mx_quantize": (_INT, [_P, _I64, _I64, _I64, _INT, _INT, _U64, _U32, _P, _P, _P]),
+    "fp4mx_hadamard_quantize": (_INT, [_P, _I64, _I64, _I64, _INT, _INT, _U32, _U64, _U32, _P, _P, _P]),
+    "fp4mx_hadamard_quantize_dual": (_INT, [_P, _I64, _I64, _I64, _INT, _U32, _U32, _INT, _U32, _U32,
+                                            _U64, _P, _P, _P, _P, _P]),
+    "fp4mx_gemm": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, C.c_float, _P, _I64, _P]),
+    "fp4mx_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "fp4mx_ctx_bytes": (_SZ, [_I64, _I64, _I64]),
+    "fp4mx_linear_fwd": (_INT, [_P, _P, _I64, _I64, _I64, _U64, _P, C.POINTER(CtxStruct), _P, _SZ, _P]),
+    "fp4mx_linear_bwd": (_INT, [_P, C.POINTER(CtxStruct), _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "fp4nv_quantize_workspace_bytes": (_SZ, [_I64, _I64]),
+    "fp4nv_quantize46": (_INT, [_P, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _SZ, _P]),
+    "fp4nv_gemm": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _SZ, _P]),
+    "fp4nv_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "fp4nv_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "fp4nv_linear_fwd": (_INT, [_P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+}
+
+EXPORTED = tuple(_SIGS)
+
+
+def lib():
+    """Load libfp4mx.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfp4mx.so is not built: run python -m fp4_microscaled_quantized_amd.build")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class Fp4mxError(RuntimeError):
+    pass
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        msg = L.fp4mx_status_string(status).decode()
+        if status == -7:
+            msg += " (hip error %d)" % L.fp4mx_last_hip_error()
+        raise Fp4mxError("fp4mx status %d: %s" % (status, msg))
+
+
+def _ptr(t: torch.Tensor):
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _bf16_2d(x: torch.Tensor):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("expected a 2-D bfloat16 CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError("innermost dimension must be contiguous")
+    return x.shape[0], x.shape[1], x.stride(0)
+
+
+def sign_mask(seed: int, gemm_id: int) -> int:
+    return int(lib().fp4mx_sign_mask(seed, gemm_id))
+
+
+@dataclass
+class MXTensor:
+    """An MXFP4 operand: codes [rows, cols/2] uint8, scales [rows, cols/32] uint8."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+
+
+def _alloc_mx(rows, cols, device):
+    return MXTensor(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                    torch.empty((rows, cols // 32), dtype=torch.uint8, device=device))
+
+
+def quantize(x, axis=ROW, rounding=RTN, seed=0, rng_stream=0, hadamard=False, mask=0) -> MXTensor:
+    """(RHT +) MXFP4 quantization of a bf16 matrix; COL returns the transposed operand."""
+    R, Cc, ld = _bf16_2d(x)
+    out = _alloc_mx(R, Cc, x.device) if axis == ROW else _alloc_mx(Cc, R, x.device)
+    L = lib()
+    if hadamard:
+        st = L.fp4mx_hadamard_quantize(_ptr(x), R, Cc, ld, axis, rounding, mask, seed, rng_stream,
+                                       _ptr(out.codes), _ptr(out.scales), _stream(x.device))
+    else:
+        st = L.fp4mx_quantize(_ptr(x), R, Cc, ld, axis, rounding, seed, rng_stream,
+                              _ptr(out.codes), _ptr(out.scales), _stream(x.device))
+    _check(st)
+    return out
+
+
+def hadamard_quantize(x, axis=ROW, rounding=RTN, mask=0, seed=0, rng_stream=0) -> MXTensor:
+    return quantize(x, axis, rounding, seed, rng_stream, hadamard=True, mask=mask)
+
+
+def hadamard_quantize_dual(x, row_rounding, row_mask, row_stream, col_rounding, col_mask,
+                           col_stream, seed=0):
+    R, Cc, ld = _bf16_2d(x)
+    ro, co = _alloc_mx(R, Cc, x.device), _alloc_mx(Cc, R, x.device)
+    _check(lib().fp4mx_hadamard_quantize_dual(
+        _ptr(x), R, Cc, ld, row_rounding, row_mask, row_stream, col_rounding, col_mask, col_stream,
+        seed, _ptr(ro.codes), _ptr(ro.scales), _ptr(co.codes), _ptr(co.scales), _stream(x.device)))
+    return ro, co
+
+
+def gemm(a: MXTensor, b: MXTensor, alpha: float = 1.0, out: torch.Tensor | None = None):
+    """C = alpha * deq(A) deq(B)^T, fp32."""
+    m, n, k = a.codes.shape[0], b.codes.shape[0], a.codes.shape[1] * 2
+    if b.codes.shape[1] * 2 != k:
+        raise ValueError("inner dimensions differ")
+    c = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=a.codes.device)
+    _check(lib().fp4mx_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), m, n, k,
+                            alpha, _ptr(c), c.stride(0), _stream(c.device)))
+    return c
+
+
+@dataclass
+class LinearCtx:
+    xt: MXTensor
+    wt: MXTensor
+    seed: int
+
+    def as_struct(self):
+        return CtxStruct(self.xt.codes.data_ptr(), self.xt.scales.data_ptr(),
+                         self.wt.codes.data_ptr(), self.wt.scales.data_ptr(), self.seed)
+
+
+def workspace(m, n, k, device):
+    nbytes = lib().fp4mx_linear_workspace_bytes(m, n, k)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def linear_fwd(x, w, seed=0, want_ctx=True, ws=None, out=None):
+    """Y = X W^T (fp32) and, when asked, the backward context."""
+    m, k, _ = _bf16_2d(x)
+    n, k2, _ = _bf16_2d(w)
+    if k2 != k or not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("x [m,k], w [n,k] contiguous")
+    dev = x.device
+    ws = ws if ws is not None else workspace(m, n, k, dev)
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    ctx = None
+    cs = None
+    if want_ctx:
+        ctx = LinearCtx(_alloc_mx(k, m, dev), _alloc_mx(k, n, dev), seed)
+        cs = C.byref(ctx.as_struct())
+    _check(lib().fp4mx_linear_fwd(_ptr(x), _ptr(w), m, n, k, seed, _ptr(y), cs, _ptr(ws),
+                                  ws.numel(), _stream(dev)))
+    return y, ctx
+
+
+def linear_bwd(dy, ctx: LinearCtx, ws=None, dx=None, dw=None):
+    """dX = 16/9 Q(dY) Q(W^T)^T, dW = 16/9 Q(dY^T) Q(X^T)^T (fp32)."""
+    m, n, _ = _bf16_2d(dy)
+    k = ctx.xt.codes.shape[0]
+    if not dy.is_contiguous():
+        raise ValueError("dy must be contiguous")
+    dev = dy.device
+    ws = ws if ws is not None else workspace(m, n, k, dev)
+    dx = dx if dx is not None else torch.empty((m, k), dtype=torch.float32, device=dev)
+    dw = dw if dw is not None else torch.empty((n, k), dtype=torch.float32, device=dev)
+    st = ctx.as_struct()
+    _check(lib().fp4mx_linear_bwd(_ptr(dy), C.byref(st), m, n, k, _ptr(dx), _ptr(dw), _ptr(ws),
+                                  ws.numel(), _stream(dev)))
+    return dx, dw
+
+
+# ------------------------------ NVFP4 --------------------------------------
+
+@dataclass
+class NVTensor:
+    """NVFP4 operand: codes [rows, cols/2], E4M3 scales [rows, cols/16], fp32 tensor scale [1]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: torch.Tensor
+
+
+def nv_quantize46(x, use_46=True) -> NVTensor:
+    R, Cc, ld = _bf16_2d(x)
+    dev = x.device
+    out = NVTensor(torch.empty((R, Cc // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((R, Cc // 16), dtype=torch.uint8, device=dev),
+                   torch.empty(1, dtype=torch.float32, device=dev))
+    ws = torch.empty(lib().fp4nv_quantize_workspace_bytes(R, Cc), dtype=torch.uint8, device=dev)
+    _check(lib().fp4nv_quantize46(_ptr(x), R, Cc, ld, int(use_46), _ptr(out.codes), _ptr(out.scales),
+                                  _ptr(out.tensor_scale), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def nv_gemm(a: NVTensor, b: NVTensor, ws=None):
+    m, n, k = a.codes.shape[0], b.codes.shape[0], a.codes.shape[1] * 2
+    dev = a.codes.device
+    if ws is None:
+        ws = torch.empty(lib().fp4nv_gemm_workspace_bytes(m, n, k), dtype=torch.uint8, device=dev)
+    c = torch.empty((m, n), dtype=torch.float32, device=dev)
+    _check(lib().fp4nv_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(a.tensor_scale), _ptr(b.codes),
+                            _ptr(b.scales), _ptr(b.tensor_scale), m, n, k, _ptr(c), n, _ptr(ws),
+                            ws.numel(), _stream(dev)))
+    return c
+
+
+def nv_linear_fwd(x, w, ws=None, out=None):
+    m, k, _ = _bf16_2d(x)
+    n, _, _ = _bf16_2d(w)
+    dev = x.device
+    if ws is None:
+        ws = torch.empty(lib().fp4nv_linear_workspace_bytes(m, n, k), dtype=torch.uint8, device=dev)
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    _check(lib().fp4nv_linear_fwd(_ptr(x), _ptr(w), m, n, k, _ptr(y), _ptr(ws), ws.numel(),
+                                  _stream(dev)))
+    return y
+
+
+# --------------------------- autograd wrapper --------------------------------
+
+class FP4LinearFunction(torch.autograd.Function):
+    """Y = X W^T with all three GEMMs in MXFP4 (fp32 outputs cast to X's dtype)."""
+
+    @staticmethod
+    def forward(ctx, x, w, seed):
+        y, c = linear_fwd(x.contiguous(), w.contiguous(), seed=int(seed), want_ctx=True)
+        ctx.fp4 = c
+        ctx.dtypes = (x.dtype, w.dtype)
+        return y.to(x.dtype)
+
+    @staticmethod
+    def backward(ctx, gy):
+        dx, dw = linear_bwd(gy.to(torch.bfloat16).contiguous(), ctx.fp4)
+        return dx.to(ctx.dtypes[0]), dw.to(ctx.dtypes[1]), None

@@ -1,0 +1,343 @@
+// extern "C" entry points of libfp4mx: argument validation, workspace
+// carving and kernel dispatch.  Every declaration, its source passage, and the
+// argument contract are in include/fp4mx.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "fp4mx_internal.h"
+
+using namespace fp4mx;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return FP4MX_E_HIP;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return FP4MX_E_DEVICE;
+  int st = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    st = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? FP4MX_OK : FP4MX_E_DEVICE;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool dim_ok(int64_t d) { return d > 0 && d % 32 == 0; }
+
+size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
+size_t mx_bytes(int64_t rows, int64_t cols) {  // codes + scales, each padded
+  return round_up((size_t)rows * cols / 2) + round_up((size_t)rows * cols / 32);
+}
+
+struct Carver {
+  uint8_t* p;
+  uint8_t* take(size_t n) {
+    uint8_t* r = p;
+    p += round_up(n);
+    return r;
+  }
+};
+
+int check_quant_args(const void* x, int64_t rows, int64_t cols, int64_t ld, int rounding,
+                     const void* codes, const void* scales) {
+  if (!x || !codes || !scales) return FP4MX_E_NULL;
+  if (!dim_ok(rows) || !dim_ok(cols) || ld < cols) return FP4MX_E_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || ld % 8 != 0) return FP4MX_E_ALIGN;
+  if (rounding != FP4MX_ROUND_RTN && rounding != FP4MX_ROUND_SR) return FP4MX_E_ARG;
+  return FP4MX_OK;
+}
+
+int quantize_impl(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis, int rounding,
+                  bool hadamard, uint32_t sign_mask, uint64_t seed, uint32_t stream_id,
+                  uint8_t* codes, uint8_t* scales, void* stream) {
+  int st = check_quant_args(x, rows, cols, ld, rounding, codes, scales);
+  if (st) return st;
+  if (axis != FP4MX_AXIS_ROW && axis != FP4MX_AXIS_COL) return FP4MX_E_ARG;
+  if ((st = check_device())) return st;
+  QuantOut o{rounding, sign_mask, make_key(seed, stream_id), codes, scales};
+  hipError_t e;
+  if (axis == FP4MX_AXIS_ROW)
+    e = launch_quant_row(static_cast<const uint16_t*>(x), rows, cols, ld, hadamard, o,
+                         (hipStream_t)stream);
+  else
+    e = launch_quant_tile(static_cast<const uint16_t*>(x), rows, cols, ld, hadamard, nullptr, &o,
+                          (hipStream_t)stream);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+int check_gemm_args(const void* a, const void* as, const void* b, const void* bs, int64_t m,
+                    int64_t n, int64_t k, const float* c, int64_t ldc) {
+  if (!a || !as || !b || !bs || !c) return FP4MX_E_NULL;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k) || ldc < n) return FP4MX_E_SHAPE;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c) || ldc % 4 != 0) return FP4MX_E_ALIGN;
+  return FP4MX_OK;
+}
+
+size_t nv_operand_bytes(int64_t rows, int64_t cols) {  // codes + e4m3 scales + tensor scale
+  return round_up((size_t)rows * cols / 2) + round_up((size_t)rows * cols / 16) + 256;
+}
+size_t nv_staged_bytes(int64_t rows, int64_t cols) {  // fp8 operand + e8m0 scales
+  return round_up((size_t)rows * cols) + round_up((size_t)rows * cols / 32);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp4mx_status_string(int status) {
+  switch (status) {
+    case FP4MX_OK: return "ok";
+    case FP4MX_E_NULL: return "null pointer";
+    case FP4MX_E_SHAPE: return "bad shape (dimensions must be positive multiples of 32)";
+    case FP4MX_E_ALIGN: return "bad alignment (16-byte pointers, leading dimension multiple of 8)";
+    case FP4MX_E_ARG: return "bad argument";
+    case FP4MX_E_WORKSPACE: return "workspace missing or too small";
+    case FP4MX_E_DEVICE: return "device is not gfx950";
+    case FP4MX_E_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int fp4mx_last_hip_error(void) { return g_last_hip_error; }
+
+uint32_t fp4mx_sign_mask(uint64_t seed, uint32_t gemm_id) {
+  return (uint32_t)splitmix64(seed ^ ((uint64_t)(0x5100u + gemm_id) << 32));
+}
+
+int fp4mx_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis, int rounding,
+                   uint64_t seed, uint32_t rng_stream, uint8_t* codes, uint8_t* scales,
+                   void* stream) {
+  return quantize_impl(x, rows, cols, ld, axis, rounding, false, 0u, seed, rng_stream, codes,
+                       scales, stream);
+}
+
+int fp4mx_hadamard_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                            int rounding, uint32_t sign_mask, uint64_t seed, uint32_t rng_stream,
+                            uint8_t* codes, uint8_t* scales, void* stream) {
+  return quantize_impl(x, rows, cols, ld, axis, rounding, true, sign_mask, seed, rng_stream, codes,
+                       scales, stream);
+}
+
+int fp4mx_hadamard_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                                 int row_rounding, uint32_t row_sign_mask, uint32_t row_rng_stream,
+                                 int col_rounding, uint32_t col_sign_mask, uint32_t col_rng_stream,
+                                 uint64_t seed, uint8_t* row_codes, uint8_t* row_scales,
+                                 uint8_t* col_codes, uint8_t* col_scales, void* stream) {
+  int st = check_quant_args(x, rows, cols, ld, row_rounding, row_codes, row_scales);
+  if (st) return st;
+  if (!col_codes || !col_scales) return FP4MX_E_NULL;
+  if (!aligned16(col_codes)) return FP4MX_E_ALIGN;
+  if (col_rounding != FP4MX_ROUND_RTN && col_rounding != FP4MX_ROUND_SR) return FP4MX_E_ARG;
+  if ((st = check_device())) return st;
+  QuantOut ro{row_rounding, row_sign_mask, make_key(seed, row_rng_stream), row_codes, row_scales};
+  QuantOut co{col_rounding, col_sign_mask, make_key(seed, col_rng_stream), col_codes, col_scales};
+  hipError_t e = launch_quant_tile(static_cast<const uint16_t*>(x), rows, cols, ld, true, &ro, &co,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+int fp4mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+               const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, float alpha, float* c,
+               int64_t ldc, void* stream) {
+  int st = check_gemm_args(a_codes, a_scales, b_codes, b_scales, m, n, k, c, ldc);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_mx_gemm(a_codes, a_scales, b_codes, b_scales, m, n, k, alpha, c, ldc,
+                                (hipStream_t)stream);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+size_t fp4mx_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
+  const size_t fwd = mx_bytes(m, k) + mx_bytes(n, k);
+  const size_t bwd = mx_bytes(m, n) + mx_bytes(n, m);
+  return fwd > bwd ? fwd : bwd;
+}
+
+size_t fp4mx_ctx_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
+  return (size_t)k * m / 2 + (size_t)k * m / 32 + (size_t)k * n / 2 + (size_t)k * n / 32;
+}
+
+int fp4mx_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t k, uint64_t seed,
+                     float* y, const fp4mx_ctx* ctx, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !w || !y) return FP4MX_E_NULL;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return FP4MX_E_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return FP4MX_E_ALIGN;
+  if (ctx) {
+    if (!ctx->xt_codes || !ctx->xt_scales || !ctx->wt_codes || !ctx->wt_scales) return FP4MX_E_NULL;
+    if (!aligned16(ctx->xt_codes) || !aligned16(ctx->wt_codes)) return FP4MX_E_ALIGN;
+    if (ctx->seed != seed) return FP4MX_E_ARG;
+  }
+  if (!ws || ws_bytes < fp4mx_linear_workspace_bytes(m, n, k)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Carver cv{static_cast<uint8_t*>(ws)};
+  uint8_t* xq = cv.take((size_t)m * k / 2);
+  uint8_t* xs = cv.take((size_t)m * k / 32);
+  uint8_t* wq = cv.take((size_t)n * k / 2);
+  uint8_t* wsc = cv.take((size_t)n * k / 32);
+  const uint32_t g0 = fp4mx_sign_mask(seed, 0), g1 = fp4mx_sign_mask(seed, 1),
+                 g2 = fp4mx_sign_mask(seed, 2);
+  QuantOut xr{FP4MX_ROUND_RTN, g0, make_key(seed, 0), xq, xs};
+  QuantOut wr{FP4MX_ROUND_RTN, g0, make_key(seed, 0), wq, wsc};
+  hipError_t e;
+  if (ctx) {
+    QuantOut xc{FP4MX_ROUND_SR, g2, make_key(seed, 4), ctx->xt_codes, ctx->xt_scales};
+    QuantOut wc{FP4MX_ROUND_SR, g1, make_key(seed, 2), ctx->wt_codes, ctx->wt_scales};
+    e = launch_quant_tile(static_cast<const uint16_t*>(x), m, k, k, true, &xr, &xc, s);
+    if (e == hipSuccess) e = launch_quant_tile(static_cast<const uint16_t*>(w), n, k, k, true, &wr, &wc, s);
+  } else {
+    e = launch_quant_row(static_cast<const uint16_t*>(x), m, k, k, true, xr, s);
+    if (e == hipSuccess) e = launch_quant_row(static_cast<const uint16_t*>(w), n, k, k, true, wr, s);
+  }
+  if (e == hipSuccess) e = launch_mx_gemm(xq, xs, wq, wsc, m, n, k, 1.0f, y, n, s);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+int fp4mx_linear_bwd(const void* dy, const fp4mx_ctx* ctx, int64_t m, int64_t n, int64_t k,
+                     float* dx, float* dw, void* ws, size_t ws_bytes, void* stream) {
+  if (!dy || !ctx || !dx || !dw) return FP4MX_E_NULL;
+  if (!ctx->xt_codes || !ctx->xt_scales || !ctx->wt_codes || !ctx->wt_scales) return FP4MX_E_NULL;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return FP4MX_E_SHAPE;
+  if (!aligned16(dy) || !aligned16(dx) || !aligned16(dw) || !aligned16(ctx->xt_codes) ||
+      !aligned16(ctx->wt_codes))
+    return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4mx_linear_workspace_bytes(m, n, k)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const uint64_t seed = ctx->seed;
+  Carver cv{static_cast<uint8_t*>(ws)};
+  uint8_t* dq = cv.take((size_t)m * n / 2);
+  uint8_t* ds = cv.take((size_t)m * n / 32);
+  uint8_t* tq = cv.take((size_t)n * m / 2);
+  uint8_t* ts = cv.take((size_t)n * m / 32);
+  QuantOut r{FP4MX_ROUND_SR, fp4mx_sign_mask(seed, 1), make_key(seed, 1), dq, ds};
+  QuantOut c{FP4MX_ROUND_SR, fp4mx_sign_mask(seed, 2), make_key(seed, 3), tq, ts};
+  const float alpha = 16.0f / 9.0f;
+  hipError_t e = launch_quant_tile(static_cast<const uint16_t*>(dy), m, n, n, true, &r, &c, s);
+  if (e == hipSuccess) e = launch_mx_gemm(dq, ds, ctx->wt_codes, ctx->wt_scales, m, k, n, alpha, dx, k, s);
+  if (e == hipSuccess) e = launch_mx_gemm(tq, ts, ctx->xt_codes, ctx->xt_scales, n, k, m, alpha, dw, k, s);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+// ------------------------------- NVFP4 -------------------------------------
+
+size_t fp4nv_quantize_workspace_bytes(int64_t rows, int64_t cols) {
+  (void)rows;
+  (void)cols;
+  return 256;
+}
+
+int fp4nv_quantize46(const void* x, int64_t rows, int64_t cols, int64_t ld, int use_46,
+                     uint8_t* codes, uint8_t* scales, float* tensor_scale, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!x || !codes || !scales || !tensor_scale) return FP4MX_E_NULL;
+  if (!dim_ok(rows) || !dim_ok(cols) || ld < cols) return FP4MX_E_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scales & 1u) || ld % 8 != 0)
+    return FP4MX_E_ALIGN;
+  if (use_46 != 0 && use_46 != 1) return FP4MX_E_ARG;
+  if (!ws || ws_bytes < fp4nv_quantize_workspace_bytes(rows, cols)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  hipError_t e = launch_nv_amax(static_cast<const uint16_t*>(x), rows, cols, ld, amax, s);
+  if (e == hipSuccess)
+    e = launch_nv_quant(static_cast<const uint16_t*>(x), rows, cols, ld, use_46, amax, codes,
+                        scales, tensor_scale, s);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+size_t fp4nv_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
+  return nv_staged_bytes(m, k) + nv_staged_bytes(n, k);
+}
+
+static int nv_gemm_impl(const uint8_t* a, const uint8_t* as, const float* ga, const uint8_t* b,
+                        const uint8_t* bs, const float* gb, int64_t m, int64_t n, int64_t k,
+                        float* c, int64_t ldc, uint8_t* ws, hipStream_t s) {
+  Carver cv{ws};
+  uint8_t* fa = cv.take((size_t)m * k);
+  uint8_t* ea = cv.take((size_t)m * k / 32);
+  uint8_t* fb = cv.take((size_t)n * k);
+  uint8_t* eb = cv.take((size_t)n * k / 32);
+  hipError_t e = launch_nv_stage(a, as, m, k, fa, ea, s);
+  if (e == hipSuccess) e = launch_nv_stage(b, bs, n, k, fb, eb, s);
+  if (e == hipSuccess) e = launch_fp8_gemm(fa, ea, fb, eb, ga, gb, m, n, k, c, ldc, s);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+int fp4nv_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+               const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale,
+               int64_t m, int64_t n, int64_t k, float* c, int64_t ldc, void* ws, size_t ws_bytes,
+               void* stream) {
+  int st = check_gemm_args(a_codes, a_scales, b_codes, b_scales, m, n, k, c, ldc);
+  if (st) return st;
+  if (!a_tensor_scale || !b_tensor_scale) return FP4MX_E_NULL;
+  if (((uintptr_t)a_scales & 1u) || ((uintptr_t)b_scales & 1u)) return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4nv_gemm_workspace_bytes(m, n, k)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  if ((st = check_device())) return st;
+  return nv_gemm_impl(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, m, n, k,
+                      c, ldc, static_cast<uint8_t*>(ws), (hipStream_t)stream);
+}
+
+size_t fp4nv_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
+  return 512 + nv_operand_bytes(m, k) + nv_operand_bytes(n, k) + fp4nv_gemm_workspace_bytes(m, n, k);
+}
+
+int fp4nv_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t k, float* y,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !w || !y) return FP4MX_E_NULL;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return FP4MX_E_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4nv_linear_workspace_bytes(m, n, k)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Carver cv{static_cast<uint8_t*>(ws)};
+  uint32_t* amax_x = reinterpret_cast<uint32_t*>(cv.take(4));
+  uint32_t* amax_w = reinterpret_cast<uint32_t*>(cv.take(4));
+  uint8_t* xq = cv.take((size_t)m * k / 2);
+  uint8_t* xs = cv.take((size_t)m * k / 16);
+  float* gx = reinterpret_cast<float*>(cv.take(4));
+  uint8_t* wq = cv.take((size_t)n * k / 2);
+  uint8_t* wsc = cv.take((size_t)n * k / 16);
+  float* gw = reinterpret_cast<float*>(cv.take(4));
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* wb = static_cast<const uint16_t*>(w);
+  hipError_t e = launch_nv_amax(xb, m, k, k, amax_x, s);
+  if (e == hipSuccess) e = launch_nv_amax(wb, n, k, k, amax_w, s);
+  if (e == hipSuccess) e = launch_nv_quant(xb, m, k, k, 1, amax_x, xq, xs, gx, s);
+  if (e == hipSuccess) e = launch_nv_quant(wb, n, k, k, 1, amax_w, wq, wsc, gw, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return nv_gemm_impl(xq, xs, gx, wq, wsc, gw, m, n, k, y, n, cv.p, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal declarations shared by the HIP translation units of libfp4mx.
+// Not part of the public ABI (see include/fp4mx.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4mx.h"
+
+namespace fp4mx {
+
+// ---------------------------------------------------------------------------
+// Host-side RNG key derivation (SplitMix64 output function; the per-element
+// generator fmix32 runs on the device).
+// ---------------------------------------------------------------------------
+inline uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+struct RngKey {
+  uint32_t lo, hi;  // the two halves of splitmix64(seed ^ (stream << 32))
+};
+
+inline RngKey make_key(uint64_t seed, uint32_t stream) {
+  uint64_t k = splitmix64(seed ^ ((uint64_t)stream << 32));
+  return RngKey{(uint32_t)k, (uint32_t)(k >> 32)};
+}
+
+// Quantizer launch description for one output operand.
+struct QuantOut {
+  int rounding;        // FP4MX_ROUND_RTN / FP4MX_ROUND_SR
+  uint32_t sign_mask;  // RHT signs (ignored when the transform is off)
+  RngKey key;          // SR stream key
+  uint8_t* codes;
+  uint8_t* scales;
+};
+
+// Launchers (defined in quant_mx.hip / gemm_mx.hip / nvfp4.hip).  They
+// assume validated arguments and return the launch's hipError_t.
+hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                            bool hadamard, const QuantOut& o, hipStream_t s);
+hipError_t launch_quant_tile(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                             bool hadamard, const QuantOut* row_out, const QuantOut* col_out,
+                             hipStream_t s);
+hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                          const uint8_t* bs, int64_t m, int64_t n, int64_t k, float alpha,
+                          float* c, int64_t ldc, hipStream_t s);
+
+hipError_t launch_nv_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                          uint32_t* amax_bits, hipStream_t s);
+hipError_t launch_nv_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                           int use_46, const uint32_t* amax_bits, uint8_t* codes,
+                           uint8_t* scales, float* tensor_scale, hipStream_t s);
+hipError_t launch_nv_stage(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                           int64_t cols, uint8_t* fp8, uint8_t* e8, hipStream_t s);
+hipError_t launch_fp8_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                           const uint8_t* bs, const float* ga, const float* gb, int64_t m,
+                           int64_t n, int64_t k, float* c, int64_t ldc, hipStream_t s);
+
+}  // namespace fp4mx

@@ -1,0 +1,238 @@
+/*
+ * fp4mx.h -- C ABI of libfp4mx.so, a fully-FP4 quantized linear layer for
+ * AMD MI355X (gfx950): block-32 randomized Hadamard transform (RHT) fused with
+ * MXFP4 quantization, the FP4 GEMMs of a linear layer's forward and backward
+ * pass, and an NVFP4 forward variant.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named x, w, dy, codes, scales, c, y, dx, dw, ws and tensor_scale
+ *   are DEVICE pointers owned by the caller.  The library never allocates or
+ *   frees memory, holds no mutable global state, and only enqueues work on
+ *   `stream` (a hipStream_t; NULL = the default stream).  Calls are
+ *   asynchronous: outputs are valid once the stream has been synchronised.
+ * - Every call returns an fp4mx_status.  Arguments are validated on the host
+ *   before any launch; on a validation error nothing is enqueued.  A HIP
+ *   launch error returns FP4MX_E_HIP and fp4mx_last_hip_error() gives the HIP
+ *   code (per calling thread).
+ * - Shapes: every dimension must be a positive multiple of 32 (FP4MX_E_SHAPE).
+ *   Pointers must be 16-byte aligned and leading dimensions (in elements) a
+ *   multiple of 8 (FP4MX_E_ALIGN).  The device must be gfx950 (FP4MX_E_DEVICE).
+ * - bf16 inputs are row-major with leading dimension `ld` (elements).
+ *
+ * MXFP4 operand layout (written by the quantizers, read by fp4mx_gemm)
+ * -------------------------------------------------------------------
+ *   codes  uint8 [rows][cols/2]  element 2j in the low nibble of byte j and
+ *          2j+1 in the high nibble; a nibble is E2M1: bit 3 sign, bits 2..0
+ *          index {0, 0.5, 1, 1.5, 2, 3, 4, 6};
+ *   scales uint8 [rows][cols/32] E8M0 (value 2^(byte-127); 0xFF marks a
+ *          group that held a non-finite value after the transform).
+ *   Every group of 32 consecutive elements along a row shares one scale:
+ *   rows are the GEMM's M (or N) index, cols its inner K index ("K-major").
+ *   Sources: "Quartet: Native FP4 Training Can Be Optimal for Large Language
+ *   Models" -- "The QuEST Forward-Pass Quantization" (groups of 32 along K,
+ *   M x ceil(K/32) scales) and "The GPU Kernel Implementation" (Stage 1, E8M0
+ *   scale from the group maximum; Stage 2 block-scaled GEMM); "Quartet II:
+ *   Accurate LLM Pre-Training in NVFP4 ..." -- "NVFP4 Format and Standard
+ *   Stochastic Rounding" (the E2M1 value set).
+ *
+ * Quantization arithmetic (bit-exact contract)
+ * --------------------------------------------
+ *   RHT: per 32-group, x'_j = -x_j if bit j of sign_mask is set; radix-2 fp32
+ *   butterflies (a,b) -> (a+b, a-b) on pairs (i, i+h), h = 1,2,4,8,16; then
+ *   y_i = t_i * fl32(1/sqrt(32)).  Scale byte e = max(biased_exponent(max|y|)
+ *   - 2, 0), i.e. 2^(e-127) = 2^(floor(log2 max|y|) - 2).
+ *   RTN: E2M1 round-to-nearest-even of y * 2^(127-e), saturating at 6.
+ *   SR:  v = fl32(y * (0.75 * 2^(127-e))) (|v| < 6 always); with a <= |v| < b
+ *        adjacent grid points, take b iff (r >> 8) * 2^-24 < (|v|-a)/(b-a),
+ *        where r = fmix32(lo32(i) ^ lo32(k) ^ fmix32(hi32(i) ^ hi32(k))),
+ *        k = splitmix64(seed ^ (rng_stream << 32)) and i = row * cols_out + col
+ *        is the element's index in the OUTPUT operand.
+ *   Sources: "Quartet: Native FP4 Training ..." -- "The Hadamard Transform:
+ *   Why It Is Necessary and How It Is Implemented" (block-32 Hadamard,
+ *   1/sqrt(g) normalisation, random sign flips, explicit seed), "The 3/4
+ *   rescaling factor" (SR(3/4 G) on the backward pass, 16/9 after the GEMM);
+ *   "Quartet II ..." -- "NVFP4 Format and Standard Stochastic Rounding" (SR
+ *   rounds up with probability (v-a)/(b-a)), "MS-EDEN" Step 1 (one random
+ *   sign pattern for all blocks of a tensor).
+ */
+#ifndef FP4MX_H
+#define FP4MX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define FP4MX_API __attribute__((visibility("default")))
+#else
+#define FP4MX_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP4MX_OK = 0,
+  FP4MX_E_NULL = -1,      /* a required pointer is NULL                       */
+  FP4MX_E_SHAPE = -2,     /* a dimension is <= 0 or not a multiple of 32      */
+  FP4MX_E_ALIGN = -3,     /* pointer not 16-B aligned / ld not multiple of 8  */
+  FP4MX_E_ARG = -4,       /* bad enum value or argument combination           */
+  FP4MX_E_WORKSPACE = -5, /* workspace NULL or smaller than required          */
+  FP4MX_E_DEVICE = -6,    /* current device is not gfx950                     */
+  FP4MX_E_HIP = -7        /* a HIP call failed; see fp4mx_last_hip_error()    */
+} fp4mx_status;
+
+enum { FP4MX_ROUND_RTN = 0, FP4MX_ROUND_SR = 1 };
+enum { FP4MX_AXIS_ROW = 0, FP4MX_AXIS_COL = 1 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+FP4MX_API const char* fp4mx_status_string(int status);
+
+/* HIP error code of this thread's last FP4MX_E_HIP (0 if none). */
+FP4MX_API int fp4mx_last_hip_error(void);
+
+/* Host helper: the 32-bit RHT sign mask shared by both operands of GEMM
+ * `gemm_id` (0 = forward Y, 1 = input gradient dX, 2 = weight gradient dW):
+ * lo32(splitmix64(seed ^ ((0x5100 + gemm_id) << 32))).  Pure host function. */
+FP4MX_API uint32_t fp4mx_sign_mask(uint64_t seed, uint32_t gemm_id);
+
+/* MXFP4-quantize one GEMM operand without a transform (y = x).
+ *   x       bf16 [rows][ld], the first `cols` columns are used.
+ *   axis    FP4MX_AXIS_ROW: groups of 32 along each row; outputs
+ *             codes [rows][cols/2], scales [rows][cols/32].
+ *           FP4MX_AXIS_COL: the operand is x^T (groups of 32 down each
+ *             column); outputs codes [cols][rows/2], scales [cols][rows/32].
+ *   rounding FP4MX_ROUND_RTN or FP4MX_ROUND_SR (SR implies the 3/4 prescale).
+ *   seed, rng_stream: the SR draw (ignored for RTN).
+ * Source: "Quartet: Native FP4 Training ..." -- "The GPU Kernel
+ * Implementation", Stage 1 (fused quantization kernel). */
+FP4MX_API int fp4mx_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                   int rounding, uint64_t seed, uint32_t rng_stream, uint8_t* codes,
+                   uint8_t* scales, void* stream);
+
+/* As fp4mx_quantize, with the block-32 RHT (sign mask `sign_mask`) applied
+ * along the grouped dimension first.  sign_mask = 0 gives the plain
+ * (deterministic) Hadamard transform.
+ * Source: "Quartet: Native FP4 Training ..." -- "The Hadamard Transform ..."
+ * and Stage 1 of "The GPU Kernel Implementation" (transform, scale and
+ * downcast fused in one kernel). */
+FP4MX_API int fp4mx_hadamard_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                            int axis, int rounding, uint32_t sign_mask, uint64_t seed,
+                            uint32_t rng_stream, uint8_t* codes, uint8_t* scales,
+                            void* stream);
+
+/* One read of x, two RHT-quantized outputs: the ROW-axis operand (groups
+ * along rows; row_* outputs [rows][cols/2], [rows][cols/32]) and the COL-axis
+ * operand (x^T; col_* outputs [cols][rows/2], [cols][rows/32]), each with its
+ * own rounding, sign mask and RNG stream (same seed).
+ * Used for the forward pass (X, W: row RTN + col SR context) and for dY
+ * (row SR + col SR).  Source: as fp4mx_hadamard_quantize; the pairing follows
+ * "The Complete Quartet Algorithm" (the backward GEMMs need both dY and dY^T). */
+FP4MX_API int fp4mx_hadamard_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                                 int row_rounding, uint32_t row_sign_mask,
+                                 uint32_t row_rng_stream, int col_rounding,
+                                 uint32_t col_sign_mask, uint32_t col_rng_stream,
+                                 uint64_t seed, uint8_t* row_codes, uint8_t* row_scales,
+                                 uint8_t* col_codes, uint8_t* col_scales, void* stream);
+
+/* C = alpha * deq(A) * deq(B)^T with fp32 accumulation and fp32 output.
+ *   A: MXFP4 operand [m][k] (a_codes [m][k/2], a_scales [m][k/32]),
+ *   B: MXFP4 operand [n][k] (b_codes [n][k/2], b_scales [n][k/32]),
+ *   C: fp32 [m][ldc], ldc >= n, ldc a multiple of 4.
+ * Source: "Quartet: Native FP4 Training ..." -- "The GPU Kernel
+ * Implementation", Stage 2 (D = C + (A x SFA)(B x SFB), FP32 accumulator). */
+FP4MX_API int fp4mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+               const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, float alpha,
+               float* c, int64_t ldc, void* stream);
+
+/* Saved forward context for the backward pass: the SR-quantized, RHT'd
+ * transposed operands X^T [k][m] (groups along m) and W^T [k][n] (groups
+ * along n), plus the seed.  All four buffers are caller-owned device memory:
+ * xt_codes k*m/2, xt_scales k*m/32, wt_codes k*n/2, wt_scales k*n/32 bytes.
+ * Source: "Quartet: Native FP4 Training ..." -- "The Complete Quartet
+ * Algorithm", Context Save (quantized tensors are saved instead of bf16). */
+typedef struct {
+  uint8_t* xt_codes;
+  uint8_t* xt_scales;
+  uint8_t* wt_codes;
+  uint8_t* wt_scales;
+  uint64_t seed;
+} fp4mx_ctx;
+
+/* Workspace bytes needed by fp4mx_linear_fwd / fp4mx_linear_bwd. */
+FP4MX_API size_t fp4mx_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
+/* Bytes of the four context buffers together. */
+FP4MX_API size_t fp4mx_ctx_bytes(int64_t m, int64_t n, int64_t k);
+
+/* Forward of the fully-FP4 linear layer Y = X W^T.
+ *   x bf16 [m][k] (ld k), w bf16 [n][k] (ld k), y fp32 [m][n].
+ *   Both operands: RHT along k with fp4mx_sign_mask(seed, 0), RTN.
+ *   ctx != NULL: also writes the backward operands from the same read of x
+ *   and w: X^T with SR, mask fp4mx_sign_mask(seed, 2), RNG stream 4; W^T with
+ *   SR, mask fp4mx_sign_mask(seed, 1), RNG stream 2; ctx->seed must equal seed.
+ *   ws: fp4mx_linear_workspace_bytes(m, n, k) bytes of device memory.
+ * Source: "Quartet: Native FP4 Training ..." -- "The Complete Quartet
+ * Algorithm", forward pass; "Quartet II ..." -- "The Complete Quartet II
+ * Computation Graph" (RHT on the inner dimension of both operands, same seed). */
+FP4MX_API int fp4mx_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t k,
+                     uint64_t seed, float* y, const fp4mx_ctx* ctx, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Backward of the fully-FP4 linear layer.
+ *   dy bf16 [m][n] (ld n) -> dx fp32 [m][k] = 16/9 Q(dY) Q(W^T)^T (inner n,
+ *   mask 1, dY rows SR with RNG stream 1) and dw fp32 [n][k] = 16/9 Q(dY^T)
+ *   Q(X^T)^T (inner m, mask 2, dY^T SR with RNG stream 3).
+ * Source: "Quartet: Native FP4 Training ..." -- "The Complete Quartet
+ * Algorithm", backward pass, and "The 3/4 rescaling factor"; "Quartet II ..."
+ * -- "The Complete Quartet II Computation Graph" (no inverse transform). */
+FP4MX_API int fp4mx_linear_bwd(const void* dy, const fp4mx_ctx* ctx, int64_t m, int64_t n,
+                     int64_t k, float* dx, float* dw, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * NVFP4 forward variant (sources: "Quartet II ..." -- "NVFP4 Format and
+ * Standard Stochastic Rounding", "MS-EDEN" Step 2 (global scale amax/(s*256)),
+ * "Forward Pass Design: ... Four-Over-Six").
+ * Operand layout: codes uint8 [rows][cols/2] (nibbles as MXFP4), scales uint8
+ * [rows][cols/16] E4M3 (OCP E4M3FN), one fp32 tensor scale g; element value
+ * q * s16 * g.  Inputs must be finite.
+ *   g = fl32(max|x| / 1536); per 16-group and c in {6, 4}:
+ *   s_c = E4M3_RNE(fl32(max|x_b| / fl32(c*g))), q = E2M1_RNE(fl32(x / fl32(s_c*g)))
+ *   (0 when s_c*g == 0), block error = pairwise fp32 sum of squared fp32
+ *   residuals; candidate 4 is kept iff its error is strictly lower (use_46 = 1).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of workspace fp4nv_quantize46 needs (amax reduction). */
+FP4MX_API size_t fp4nv_quantize_workspace_bytes(int64_t rows, int64_t cols);
+
+/* NVFP4 RTN (+4/6) quantization of x bf16 [rows][ld] along rows.
+ * tensor_scale: device pointer to one float (written).  cols % 32 == 0. */
+FP4MX_API int fp4nv_quantize46(const void* x, int64_t rows, int64_t cols, int64_t ld, int use_46,
+                     uint8_t* codes, uint8_t* scales, float* tensor_scale, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* C = deq(A) deq(B)^T (fp32 [m][ldc]) for NVFP4 operands A [m][k], B [n][k].
+ * Each 32-element K block is staged to FP8 E4M3: e_blk = max exponent of the
+ * block's two E4M3 scales - 5 (0 if both are 0), element = E4M3_RNE(q * s16 *
+ * 2^-e_blk), and fed to the scaled FP8 MFMA with the E8M0 block scale
+ * 2^e_blk; the epilogue multiplies by fl32(g_A * g_B). */
+FP4MX_API int fp4nv_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+               const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale,
+               int64_t m, int64_t n, int64_t k, float* c, int64_t ldc, void* ws,
+               size_t ws_bytes, void* stream);
+
+/* Workspace bytes for fp4nv_gemm (FP8-staged operands) and fp4nv_linear_fwd. */
+FP4MX_API size_t fp4nv_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+FP4MX_API size_t fp4nv_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* Y = X W^T with both operands NVFP4 RTN + 4/6 quantized (x [m][k], w [n][k]
+ * bf16 with ld k; y fp32 [m][n]). */
+FP4MX_API int fp4nv_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t k,
+                     float* y, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4MX_H */

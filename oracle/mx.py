@@ -36,7 +36,7 @@ def _scale_inv(code: np.ndarray) -> np.ndarray:
 
 
 def quantize(x: np.ndarray, *, rounding: int, axis: int = ROW, hadamard: bool = True,
-             sign_mask: int = 0, seed: int = 0, stream: int = 0):
+             sign_mask: int = 0, seed: int = 0, stream: int = 0, row_ids=None):
     """MXFP4-quantize one GEMM operand.
 
     x        float32 [R, C] holding bfloat16 values.
@@ -56,6 +56,9 @@ def quantize(x: np.ndarray, *, rounding: int, axis: int = ROW, hadamard: bool = 
     A group holding a non-finite value (after the transform) gets scale 0xFF
     and all-zero element codes.
     The SR draw for output element (r, c) uses index r * cols_out + c.
+    ``row_ids`` (optional) gives the output rows' indices in the full operand
+    when only some of its rows are passed (sampled checks); the rows are
+    independent, so this is the same computation restricted to those rows.
     """
     a = np.asarray(x, dtype=np.float32)
     if axis == COL:
@@ -76,7 +79,8 @@ def quantize(x: np.ndarray, *, rounding: int, axis: int = ROW, hadamard: bool = 
     elif rounding == SR:
         f = (np.float32(0.75) * inv).astype(np.float32)      # exact: 3 * 2^(125-e)
         v = (blocks * f).astype(np.float32)
-        idx = (np.arange(R, dtype=np.uint64)[:, None] * np.uint64(C)
+        rid = np.arange(R, dtype=np.uint64) if row_ids is None else np.asarray(row_ids, dtype=np.uint64)
+        idx = (rid[:, None] * np.uint64(C)
                + np.arange(C, dtype=np.uint64)[None, :]).reshape(R, C // 32, 32)
         u = rng.uniform24(rng.bits(seed, stream, idx))
         v = np.where(finite[:, :, None], v, 0).astype(np.float32)

@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before touching a GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from fp4_microscaled_quantized_amd import binding
+from oracle import rng
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4mx.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"FP4MX_API\s+[\w\s\*]*?\b(fp4(?:mx|nv)_\w+)\s*\(", txt)))
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for want in ("fp4mx_quantize", "fp4mx_hadamard_quantize", "fp4mx_gemm", "fp4mx_linear_fwd",
+                 "fp4mx_linear_bwd", "fp4nv_quantize46", "fp4nv_gemm", "fp4nv_linear_fwd"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert set(_declared()) == set(binding.EXPORTED)
+
+
+def test_sign_mask_matches_oracle():
+    L = binding.lib()
+    for seed in (0, 1, 12345, 2 ** 63 + 7):
+        for g in range(3):
+            assert L.fp4mx_sign_mask(seed, g) == rng.sign_mask(seed, g)
+
+
+def test_workspace_sizes():
+    L = binding.lib()
+    assert L.fp4mx_linear_workspace_bytes(0, 32, 32) == 0
+    assert L.fp4mx_linear_workspace_bytes(33, 32, 32) == 0
+    m, n, k = 8192, 14336, 4096
+    ws = L.fp4mx_linear_workspace_bytes(m, n, k)
+    # forward: codes + scales of X and W (4.25 bits/element); backward: dY and dY^T
+    assert ws >= max((m * k + n * k) * 17 // 32, 2 * m * n * 17 // 32)
+    assert L.fp4mx_ctx_bytes(m, n, k) == (k * m + k * n) * 17 // 32
+    assert L.fp4nv_gemm_workspace_bytes(64, 64, 64) >= 2 * 64 * 64 * 33 // 32
+
+
+def _buf(n=4096):
+    b = C.create_string_buffer(n + 64)
+    addr = (C.addressof(b) + 63) & ~63
+    return b, C.c_void_p(addr)
+
+
+@pytest.mark.parametrize("case", ["null", "shape", "ld", "align", "round", "axis"])
+def test_quantize_validation(case):
+    L = binding.lib()
+    keep, p = _buf()
+    args = dict(x=p, rows=64, cols=64, ld=64, axis=0, rnd=0, codes=p, scales=p)
+    want = {"null": -1, "shape": -2, "ld": -3, "align": -3, "round": -4, "axis": -4}[case]
+    if case == "null":
+        args["x"] = None
+    elif case == "shape":
+        args["cols"] = 48
+    elif case == "ld":
+        args["ld"] = 68
+    elif case == "align":
+        args["codes"] = C.c_void_p(p.value + 4)
+    elif case == "round":
+        args["rnd"] = 5
+    elif case == "axis":
+        args["axis"] = 3
+    st = L.fp4mx_quantize(args["x"], args["rows"], args["cols"], args["ld"], args["axis"], args["rnd"],
+                          0, 0, args["codes"], args["scales"], None)
+    assert st == want
+    assert L.fp4mx_status_string(st)
+
+
+def test_gemm_and_linear_validation():
+    L = binding.lib()
+    keep, p = _buf()
+    f = C.c_void_p(p.value)
+    assert L.fp4mx_gemm(p, p, p, p, 64, 64, 0, 1.0, f, 64, None) == -2
+    assert L.fp4mx_gemm(p, p, p, p, 64, 64, 64, 1.0, f, 60, None) == -2      # ldc < n
+    assert L.fp4mx_gemm(None, p, p, p, 64, 64, 64, 1.0, f, 64, None) == -1
+    # workspace too small
+    ctx = binding.CtxStruct(p.value, p.value, p.value, p.value, 3)
+    assert L.fp4mx_linear_fwd(p, p, 64, 64, 64, 3, f, C.byref(ctx), p, 16, None) == -5
+    # context seed must match the call's seed
+    assert L.fp4mx_linear_fwd(p, p, 64, 64, 64, 4, f, C.byref(ctx), p, 1 << 20, None) == -4
+    assert L.fp4mx_linear_bwd(p, None, 64, 64, 64, f, f, p, 1 << 20, None) == -1
+    assert L.fp4nv_quantize46(p, 64, 64, 64, 2, p, p, f, p, 256, None) == -4
+    assert L.fp4nv_linear_fwd(p, p, 64, 64, 64, f, p, 0, None) == -5
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libfp4mx.so")
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError):
+        binding.lib()

@@ -1,0 +1,71 @@
+"""GPU parity: the MXFP4 GEMM against the oracle's float64 dequantized product."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_microscaled_quantized_amd as fq
+from fp4_microscaled_quantized_amd import synth
+from oracle import mx
+
+from gpu_util import cpu, dev_bf16, host_f32, log, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5   # relative Frobenius error against the fp64 product
+
+
+def _operands(m, n, k, seed=0):
+    a = synth.normal_with_outliers((m, k), seed, 0)
+    b = synth.normal((n, k), 0.02, seed, 1)
+    return a, b
+
+
+def _to_dev_mx(codes, scales):
+    return fq.MXTensor(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 128, 128), (32, 32, 32), (96, 160, 320), (128, 128, 256),
+                                   (256, 384, 1024), (160, 96, 288), (512, 256, 2048)])
+def test_gemm_parity(m, n, k):
+    log("gemm", m, n, k)
+    a, b = _operands(m, n, k)
+    qa = mx.quantize(host_f32(a), rounding=mx.RTN, sign_mask=3)
+    qb = mx.quantize(host_f32(b), rounding=mx.SR, sign_mask=3, seed=1, stream=2)
+    c = fq.gemm(_to_dev_mx(*qa), _to_dev_mx(*qb), alpha=1.5)
+    torch.cuda.synchronize()
+    want = mx.gemm(*qa, *qb, alpha=1.5)
+    err = rel_fro(cpu(c), want)
+    log("  rel err", err)
+    assert err <= TOL
+
+
+def test_gemm_output_stride_and_alpha():
+    a, b = _operands(64, 96, 256)
+    qa = mx.quantize(host_f32(a), rounding=mx.RTN)
+    qb = mx.quantize(host_f32(b), rounding=mx.RTN)
+    out = torch.full((64, 128), 7.0, dtype=torch.float32, device="cuda")
+    fq.gemm(_to_dev_mx(*qa), _to_dev_mx(*qb), alpha=16 / 9, out=out)
+    torch.cuda.synchronize()
+    o = cpu(out)
+    assert np.all(o[:, 96:] == 7.0)               # columns beyond n untouched
+    assert rel_fro(o[:, :96], mx.gemm(*qa, *qb, alpha=16 / 9)) <= TOL
+
+
+def test_gemm_nan_scale_propagates():
+    a, b = _operands(64, 64, 128)
+    qa = list(mx.quantize(host_f32(a), rounding=mx.RTN))
+    qb = mx.quantize(host_f32(b), rounding=mx.RTN)
+    qa[1] = qa[1].copy()
+    qa[1][3, 1] = 255                              # non-finite group in row 3
+    c = cpu(fq.gemm(_to_dev_mx(*qa), _to_dev_mx(*qb)))
+    assert np.all(np.isnan(c[3]))
+    assert np.all(np.isfinite(np.delete(c, 3, axis=0)))
+
+
+def test_gemm_extreme_scales():
+    # products spanning the E8M0 range stay exact in fp32 accumulation
+    rs = np.random.default_rng(0)
+    qa = (rs.integers(0, 256, (64, 64), dtype=np.uint8), rs.integers(100, 150, (64, 4)).astype(np.uint8))
+    qb = (rs.integers(0, 256, (32, 64), dtype=np.uint8), rs.integers(100, 150, (32, 4)).astype(np.uint8))
+    c = cpu(fq.gemm(_to_dev_mx(*qa), _to_dev_mx(*qb)))
+    assert rel_fro(c, mx.gemm(*qa, *qb)) <= TOL

@@ -1,0 +1,124 @@
+"""GPU parity of the fully-FP4 linear layer (forward + backward) against the oracle.
+
+Small shapes are compared in full; the Quartet-style (8192 x 4096 x 4096) and
+Llama-3-8B FFN-up (8192 x 4096 -> 14336) workloads are checked at full size,
+with the entry points the benchmark times, on sampled outputs whose oracle
+operands are computed row by row."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_microscaled_quantized_amd as fq
+from fp4_microscaled_quantized_amd import synth
+from oracle import mx, rng
+
+from gpu_util import assert_bytes_equal, cpu, dev_bf16, host_f32, log, rel_fro
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _run(xb, wb, dyb, seed):
+    x, w, dy = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb)
+    y, ctx = fq.linear_fwd(x, w, seed=seed)
+    dx, dw = fq.linear_bwd(dy, ctx)
+    torch.cuda.synchronize()
+    return y, ctx, dx, dw
+
+
+def test_tiny_forward_workload():
+    """X 64x128, W 128x128, N(0,1) with 1% x20 outliers, seeded RHT, RTN, Y fp32."""
+    d = synth.tiny_linear(0)
+    for seed in (0, 9):
+        y, _ = fq.linear_fwd(dev_bf16(d["x"]), dev_bf16(d["w"]), seed=seed, want_ctx=False)
+        want, _ = mx.linear_fwd(host_f32(d["x"]), host_f32(d["w"]), seed, want_ctx=False)
+        err = rel_fro(cpu(y), want)
+        log("tiny fwd seed", seed, "rel err", err)
+        assert err <= TOL
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 96, 160), (64, 64, 64), (256, 384, 512), (96, 32, 224)])
+def test_forward_backward_small(m, n, k):
+    log("linear", m, n, k)
+    xb = synth.normal((m, k), 1.0, 3, 0)
+    wb = synth.normal((n, k), 0.02, 3, 1)
+    dyb = synth.normal((m, n), 1e-3, 3, 2)
+    seed = 17
+    y, ctx, dx, dw = _run(xb, wb, dyb, seed)
+    xf, wf, dyf = host_f32(xb), host_f32(wb), host_f32(dyb)
+    ry, rctx = mx.linear_fwd(xf, wf, seed)
+    assert_bytes_equal(cpu(ctx.xt.codes), rctx["xt"][0], "ctx xt codes")
+    assert_bytes_equal(cpu(ctx.xt.scales), rctx["xt"][1], "ctx xt scales")
+    assert_bytes_equal(cpu(ctx.wt.codes), rctx["wt"][0], "ctx wt codes")
+    assert_bytes_equal(cpu(ctx.wt.scales), rctx["wt"][1], "ctx wt scales")
+    rdx, rdw = mx.linear_bwd(dyf, rctx)
+    for name, got, want in (("y", y, ry), ("dx", dx, rdx), ("dw", dw, rdw)):
+        err = rel_fro(cpu(got), want)
+        log("  ", name, "rel err", err)
+        assert err <= TOL
+
+
+def test_backward_unbiased_on_gpu():
+    """Mean of B independent GPU backward estimates -> exact gradient, error ~ 1/B."""
+    m, n, k = 64, 64, 128
+    xb = synth.normal((m, k), 1.0, 4, 0)
+    wb = synth.normal((n, k), 1.0, 4, 1)
+    dyb = synth.normal((m, n), 1.0, 4, 2)
+    x, w, dy = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb)
+    ex_dx = host_f32(dyb).astype(np.float64) @ host_f32(wb).astype(np.float64)
+    ex_dw = host_f32(dyb).T.astype(np.float64) @ host_f32(xb).astype(np.float64)
+    dxs, dws = [], []
+    for seed in range(256):
+        _, ctx = fq.linear_fwd(x, w, seed=seed)
+        dx, dw = fq.linear_bwd(dy, ctx)
+        dxs.append(cpu(dx))
+        dws.append(cpu(dw))
+    for ests, ex in ((np.array(dxs), ex_dx), (np.array(dws), ex_dw)):
+        def mse(B):
+            mm = ests[: (len(ests) // B) * B].reshape(-1, B, *ex.shape).mean(axis=1)
+            return np.mean((mm - ex) ** 2)
+        e1, e16, e64 = mse(1), mse(16), mse(64)
+        log("  1/B mse", e1, e16, e64)
+        assert e16 < e1 / 8 and e64 < e1 / 30
+
+
+def _sampled_full_size(d, seed, nsamp=48):
+    x, w, dy = d["x"], d["w"], d["dy"]
+    m, k = x.shape
+    n = w.shape[0]
+    log("full-size linear", m, n, k)
+    y, ctx, dx, dw = _run(x, w, dy, seed)
+    rs = np.random.default_rng(123)
+    ri = np.sort(rs.choice(m, nsamp, replace=False))   # rows of Y / dX
+    cj = np.sort(rs.choice(n, nsamp, replace=False))   # cols of Y / rows of dW
+    ck = np.sort(rs.choice(k, nsamp, replace=False))   # cols of dX / dW
+    xf, wf, dyf = host_f32(x), host_f32(w), host_f32(dy)
+    g0, g1, g2 = (rng.sign_mask(seed, i) for i in range(3))
+    # Y[ri, cj]: rows of Q_RTN(RHT_K X) and Q_RTN(RHT_K W)
+    qx = mx.quantize(xf[ri], rounding=mx.RTN, sign_mask=g0)
+    qw = mx.quantize(wf[cj], rounding=mx.RTN, sign_mask=g0)
+    ey = rel_fro(cpu(y)[np.ix_(ri, cj)], mx.gemm(*qx, *qw))
+    # context rows: W^T rows ck (W columns, SR along N, stream 2) and X^T rows ck
+    wt = mx.quantize(wf[:, ck], rounding=mx.SR, axis=mx.COL, sign_mask=g1, seed=seed, stream=2, row_ids=ck)
+    xt = mx.quantize(xf[:, ck], rounding=mx.SR, axis=mx.COL, sign_mask=g2, seed=seed, stream=4, row_ids=ck)
+    assert_bytes_equal(cpu(ctx.wt.codes)[ck], wt[0], "ctx wt codes (sampled rows)")
+    assert_bytes_equal(cpu(ctx.wt.scales)[ck], wt[1], "ctx wt scales (sampled rows)")
+    assert_bytes_equal(cpu(ctx.xt.codes)[ck], xt[0], "ctx xt codes (sampled rows)")
+    assert_bytes_equal(cpu(ctx.xt.scales)[ck], xt[1], "ctx xt scales (sampled rows)")
+    # dX[ri, ck] = 16/9 Q_SR(RHT_N dY)[ri] . W^T[ck]
+    qdy = mx.quantize(dyf[ri], rounding=mx.SR, sign_mask=g1, seed=seed, stream=1, row_ids=ri)
+    edx = rel_fro(cpu(dx)[np.ix_(ri, ck)], mx.gemm(*qdy, *wt, alpha=16 / 9))
+    # dW[cj, ck] = 16/9 Q_SR(RHT_M dY^T)[cj] . X^T[ck]
+    qdyt = mx.quantize(dyf[:, cj], rounding=mx.SR, axis=mx.COL, sign_mask=g2, seed=seed, stream=3,
+                       row_ids=cj)
+    edw = rel_fro(cpu(dw)[np.ix_(cj, ck)], mx.gemm(*qdyt, *xt, alpha=16 / 9))
+    log("  sampled rel err y %.2e dx %.2e dw %.2e" % (ey, edx, edw))
+    assert ey <= TOL and edx <= TOL and edw <= TOL
+
+
+def test_quartet_workload_full_size():
+    _sampled_full_size(synth.quartet_linear(0), seed=0)
+
+
+def test_llama_ffn_up_workload_full_size():
+    _sampled_full_size(synth.llama_ffn_up(0), seed=0)
