@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark of the fully-FP4 (MXFP4) linear layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+forward (RHT + RTN quantization of X and W fused with the SR context, FP4
+GEMM Y = X W^T) and backward (RHT + SR quantization of dY and dY^T, FP4 GEMMs
+dX and dW), i.e. the kernels fp4mx_linear_fwd + fp4mx_linear_bwd launch,
+called here one by one through the C ABI so that each launch is bracketed by
+HIP events on the stream it runs on.
+
+Headline workload: Quartet-style layer, 8192 tokens, d_in = d_out = 4096.
+value = 6*M*N*K flop / step time (TFLOP/s).  Printed as one JSON line.
+
+Extra fields (same line): the Llama-3-8B FFN-up layer (8192 x 4096 -> 14336),
+the stand-alone quantizer on the 8192 x 4096 workload (GB/s, HBM roofline,
+rotating input buffers so the 256 MB Infinity Cache cannot hold them), the
+NVFP4 forward variant (16384 x 8192 -> 8192), and the CPU oracle timed on a
+bounded sample (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP4 linear fwd+bwd TFLOPS (% FP4 MFMA peak); quantizer GB/s (% HBM)"
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+MX_BYTES_PER_ELEM = 2 + 0.5 + 1 / 32   # bf16 in, 4-bit code + 1/32 scale byte out
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", choices=["quartet", "llama"], default="quartet")
+    p.add_argument("--no-extra", action="store_true", help="only the headline workload")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run one 512 MiB device copy (traffic counter calibration)")
+    return p.parse_args()
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class LinearStep:
+    """The MXFP4 linear fwd+bwd hot path through the C ABI, with per-launch events."""
+
+    def __init__(self, d, seed=0):
+        import torch
+        import fp4_microscaled_quantized_amd as fq
+        self.fq = fq
+        self.x, self.w, self.dy = dev_bf16(d["x"]), dev_bf16(d["w"]), dev_bf16(d["dy"])
+        self.m, self.k = self.x.shape
+        self.n = self.w.shape[0]
+        self.seed = seed
+        m, n, k = self.m, self.n, self.k
+        dev = self.x.device
+        e = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+        self.xq, self.xs, self.xtq, self.xts = e(m, k // 2), e(m, k // 32), e(k, m // 2), e(k, m // 32)
+        self.wq, self.wsc, self.wtq, self.wts = e(n, k // 2), e(n, k // 32), e(k, n // 2), e(k, n // 32)
+        self.dq, self.ds, self.dtq, self.dts = e(m, n // 2), e(m, n // 32), e(n, m // 2), e(n, m // 32)
+        f = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+        self.y, self.dx, self.dw = f(m, n), f(m, k), f(n, k)
+        self.g = [fq.sign_mask(seed, i) for i in range(3)]
+        self.names = ["quant_x", "quant_w", "gemm_y", "quant_dy", "gemm_dx", "gemm_dw"]
+        self.times = {nm: [] for nm in self.names}
+
+    def _calls(self):
+        fq, L, C = self.fq, self.fq.lib(), None
+        from fp4_microscaled_quantized_amd.binding import _check, _ptr, _stream
+        s = _stream()
+        m, n, k, seed = self.m, self.n, self.k, self.seed
+        g0, g1, g2 = self.g
+        RTN, SR = fq.RTN, fq.SR
+        return [
+            lambda: _check(L.fp4mx_hadamard_quantize_dual(_ptr(self.x), m, k, k, RTN, g0, 0, SR, g2, 4, seed,
+                                                          _ptr(self.xq), _ptr(self.xs), _ptr(self.xtq),
+                                                          _ptr(self.xts), s)),
+            lambda: _check(L.fp4mx_hadamard_quantize_dual(_ptr(self.w), n, k, k, RTN, g0, 0, SR, g1, 2, seed,
+                                                          _ptr(self.wq), _ptr(self.wsc), _ptr(self.wtq),
+                                                          _ptr(self.wts), s)),
+            lambda: _check(L.fp4mx_gemm(_ptr(self.xq), _ptr(self.xs), _ptr(self.wq), _ptr(self.wsc), m, n, k,
+                                        1.0, _ptr(self.y), n, s)),
+            lambda: _check(L.fp4mx_hadamard_quantize_dual(_ptr(self.dy), m, n, n, SR, g1, 1, SR, g2, 3, seed,
+                                                          _ptr(self.dq), _ptr(self.ds), _ptr(self.dtq),
+                                                          _ptr(self.dts), s)),
+            lambda: _check(L.fp4mx_gemm(_ptr(self.dq), _ptr(self.ds), _ptr(self.wtq), _ptr(self.wts), m, k, n,
+                                        16.0 / 9.0, _ptr(self.dx), k, s)),
+            lambda: _check(L.fp4mx_gemm(_ptr(self.dtq), _ptr(self.dts), _ptr(self.xtq), _ptr(self.xts), n, k, m,
+                                        16.0 / 9.0, _ptr(self.dw), k, s)),
+        ]
+
+    def run(self, steps, timed):
+        import torch
+        calls = self._calls()
+        evs = []
+        for _ in range(steps):
+            if timed:
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+                ev[0].record()
+                for i, c in enumerate(calls):
+                    c()
+                    ev[i + 1].record()
+                evs.append(ev)
+            else:
+                for c in calls:
+                    c()
+        return evs
+
+    def collect(self, evs):
+        for ev in evs:
+            for i, nm in enumerate(self.names):
+                self.times[nm].append(ev[i].elapsed_time(ev[i + 1]))
+
+    def check_against_composite(self):
+        """The decomposed calls must reproduce fp4mx_linear_fwd / _bwd bit for bit."""
+        import torch
+        fq = self.fq
+        self.run(1, False)
+        y, ctx = fq.linear_fwd(self.x, self.w, seed=self.seed)
+        dx, dw = fq.linear_bwd(self.dy, ctx)
+        torch.cuda.synchronize()
+        ok = (torch.equal(y, self.y) and torch.equal(dx, self.dx) and torch.equal(dw, self.dw)
+              and torch.equal(ctx.xt.codes, self.xtq) and torch.equal(ctx.wt.scales, self.wts))
+        if not ok:
+            raise SystemExit("decomposed step differs from fp4mx_linear_fwd/bwd")
+
+    def flops(self):
+        return 6.0 * self.m * self.n * self.k
+
+
+def time_linear(d, steps, warmup, seed=0):
+    import torch
+    st = LinearStep(d, seed)
+    st.check_against_composite()
+    st.run(warmup, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs = st.run(steps, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st.collect(evs)
+    avg = {nm: float(np.mean(v)) for nm, v in st.times.items()}
+    return st, wall, avg
+
+
+def gemm_roofline(st, avg):
+    """FP4 MFMA roofline of the GEMM kernel: 2MNK flop per launch / mean launch time."""
+    m, n, k = st.m, st.n, st.k
+    fl = {"gemm_y": 2.0 * m * n * k, "gemm_dx": 2.0 * m * k * n, "gemm_dw": 2.0 * n * k * m}
+    tot_fl = sum(fl.values())
+    tot_ms = sum(avg[x] for x in fl)
+    achieved = tot_fl / (tot_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": "mx_gemm_kernel (FP4 32x32x64 scaled MFMA)",
+            "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": None,
+            "per_launch_ms": {x: round(avg[x], 4) for x in fl}}
+
+
+def quant_roofline(st, avg):
+    m, n, k = st.m, st.n, st.k
+    # dual quantizer: 2 B read + two outputs of 0.5 + 1/32 B per element
+    by = {"quant_x": m * k * (2 + 2 * (0.5 + 1 / 32)), "quant_w": n * k * (2 + 2 * (0.5 + 1 / 32)),
+          "quant_dy": m * n * (2 + 2 * (0.5 + 1 / 32))}
+    gbs = sum(by.values()) / (sum(avg[x] for x in by) * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def time_quantizer(steps, warmup, nbuf=6):
+    """fp4mx_hadamard_quantize (row axis) on the 8192 x 4096 workload, RTN and SR."""
+    import torch
+    import fp4_microscaled_quantized_amd as fq
+    from fp4_microscaled_quantized_amd import synth
+    from fp4_microscaled_quantized_amd.binding import _check, _ptr, _stream
+    x0 = dev_bf16(synth.quantizer_tensor()["x"])
+    R, Cc = x0.shape
+    xs = [x0] + [x0.clone() for _ in range(nbuf - 1)]
+    outs = [(torch.empty((R, Cc // 2), dtype=torch.uint8, device="cuda"),
+             torch.empty((R, Cc // 32), dtype=torch.uint8, device="cuda")) for _ in range(nbuf)]
+    L = fq.lib()
+    mask = fq.sign_mask(0, 0)
+    res = {}
+    for name, rnd in (("rtn", fq.RTN), ("sr", fq.SR)):
+        def call(i):
+            _check(L.fp4mx_hadamard_quantize(_ptr(xs[i % nbuf]), R, Cc, Cc, fq.ROW, rnd, mask, 0, 1,
+                                             _ptr(outs[i % nbuf][0]), _ptr(outs[i % nbuf][1]), _stream()))
+        for i in range(warmup):
+            call(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            call(i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+        byt = R * Cc * MX_BYTES_PER_ELEM
+        gbs = byt / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                     "bytes_per_launch": int(byt)}
+    return {"workload": "quantizer 8192x4096 bf16, half N(0,1) half Student-t(3), RHT-32, row axis",
+            "rotating_buffers_MB": round(nbuf * (R * Cc * 2 + R * Cc * 17 // 32) / 1e6, 1), **res}
+
+
+def time_nvfp4(steps, warmup):
+    import torch
+    import fp4_microscaled_quantized_amd as fq
+    from fp4_microscaled_quantized_amd import synth
+    d = synth.nvfp4_linear(0)
+    x, w = dev_bf16(d["x"]), dev_bf16(d["w"])
+    m, k = x.shape
+    n = w.shape[0]
+    ws = torch.empty(fq.lib().fp4nv_linear_workspace_bytes(m, n, k), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        fq.nv_linear_fwd(x, w, ws=ws, out=y)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        fq.nv_linear_fwd(x, w, ws=ws, out=y)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    return {"workload": "NVFP4 RTN+4/6 linear fwd 16384x8192->8192", "ms": round(ms, 4),
+            "TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+
+
+def cpu_baseline(rows=256):
+    """The oracle's linear fwd+bwd on the first `rows` tokens of the headline workload."""
+    from fp4_microscaled_quantized_amd import synth
+    from oracle import mx, rng
+    d = synth.quartet_linear(0)
+    f = synth.bf16_bits_to_f32
+    x, w, dy = f(d["x"][:rows]), f(d["w"]), f(d["dy"][:rows])
+    n, k = w.shape
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    t0 = time.perf_counter()
+    y, ctx = mx.linear_fwd(x, w, seed=0)
+    dx, dw = mx.linear_bwd(dy, ctx)
+    dt = time.perf_counter() - t0
+    flop = 6.0 * rows * n * k
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
+            "sample": "linear fwd+bwd on the first %d of 8192 token rows of the 8192x4096x4096 workload "
+                      "(6*%d*4096*4096 flop) in %.1f s; numpy elementwise on 1 thread, fp64 matmul on %d "
+                      "BLAS threads" % (rows, rows, dt, blas)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from fp4_microscaled_quantized_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if a.calib_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    if a.workload == "quartet":
+        d = synth.quartet_linear(0)
+        wl = {"workload": "quartet_linear fwd+bwd M=8192 N=4096 K=4096", "m": 8192, "n": 4096, "k": 4096}
+    else:
+        d = synth.llama_ffn_up(0)
+        wl = {"workload": "llama3_8b_ffn_up fwd+bwd M=8192 K=4096 N=14336", "m": 8192, "n": 14336, "k": 4096}
+    st, wall, avg = time_linear(d, a.steps, a.warmup)
+    ev_ms = sum(avg.values())
+    ms_step = wall * 1e3 / a.steps
+    value = st.flops() / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
+        "data": "synthetic", "config": {**wl, "seed": 0, "parallelism": "none (1 GPU)"},
+        "frac_fp4_peak": round(value / PEAK_FP4_TFLOPS, 4),
+        "roofline": gemm_roofline(st, avg),
+        "breakdown_ms": {k2: round(v, 4) for k2, v in avg.items()},
+        "event_sum_ms_per_step": round(ev_ms, 4),
+        "quantizer_roofline_in_step": quant_roofline(st, avg),
+    }
+    del st
+    torch.cuda.empty_cache()
+    if not a.no_extra:
+        if a.workload == "quartet":
+            st2, wall2, avg2 = time_linear(synth.llama_ffn_up(0), a.steps, a.warmup)
+            ms2 = wall2 * 1e3 / a.steps
+            out["llama_ffn_up"] = {"workload": "8192 x 4096 -> 14336 fwd+bwd", "ms_per_step": round(ms2, 4),
+                                   "TFLOP/s": round(st2.flops() / (ms2 * 1e-3) / 1e12, 1),
+                                   "gemm_roofline": gemm_roofline(st2, avg2),
+                                   "breakdown_ms": {k2: round(v, 4) for k2, v in avg2.items()}}
+            del st2
+            torch.cuda.empty_cache()
+        out["quantizer"] = time_quantizer(max(a.steps, 20), a.warmup)
+        torch.cuda.empty_cache()
+        out["nvfp4"] = time_nvfp4(max(a.steps // 2, 5), 2)
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
