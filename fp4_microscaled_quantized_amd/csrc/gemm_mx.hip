@@ -36,6 +36,13 @@
 
 #include "fp4mx_internal.h"
 
+#ifndef FP4MX_GEMM_WM
+#define FP4MX_GEMM_WM 2  // waves along M
+#endif
+#ifndef FP4MX_GEMM_WN
+#define FP4MX_GEMM_WN 2  // waves along N
+#endif
+
 namespace fp4mx {
 namespace {
 
@@ -44,14 +51,27 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256, kBN = 256, kThreads = 256;
+constexpr int kBM = 256, kBN = 256;
 constexpr int kRowBytes = 128;              // operand bytes per row per stage
-constexpr int kPitch = kRowBytes + 16;      // padded LDS row
-constexpr int kCodeLds = (kBM + kBN) * kPitch;
+constexpr int kCodeLds = (kBM + kBN) * kRowBytes;
 constexpr int kScaleLds = (kBM + kBN) * 8;
 constexpr int kStageLds = kCodeLds + kScaleLds;
-constexpr int kLoads = (kBM + kBN) * (kRowBytes / 16) / kThreads;  // 16 per thread
 constexpr uint32_t kOOB = 0x80000000u;      // offset beyond any num_records
+
+// Wave layout: WM x WN waves, each owning a (256/WM) x (256/WN) sub-tile.
+template <int WM, int WN>
+struct Waves {
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int FM = kBM / WM / 32, FN = kBN / WN / 32;  // 32x32 fragments per wave
+  static constexpr int kBlocks = kCodeLds / 1024 / kWaves;      // 1-KB LDS blocks per wave per stage
+  static constexpr int kMinWaves = kWaves / 4;                  // waves per SIMD
+};
+
+// LDS operand layout: row r of a 256-row operand tile holds its 128 stage
+// bytes as eight 16-B chunks; chunk c is stored in slot c ^ ((r >> 1) & 7), so
+// the 16-B fragment reads of 16 consecutive rows touch all 64 banks once.
+__device__ __forceinline__ int lds_slot(int r, int c) { return r * kRowBytes + ((c ^ ((r >> 1) & 7)) << 4); }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -73,6 +93,12 @@ __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+// 16 B per lane straight into LDS: lane l's data lands at lds + 16 l (the
+// wave writes one contiguous 1-KB block); out-of-range offsets write zeros.
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
 }
 __device__ __forceinline__ void buf_store4(float v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
@@ -100,16 +126,19 @@ __device__ __forceinline__ void tile_of(int wg, int gm, int gn, int& tm, int& tn
   tn = r / gsz;
 }
 
-template <int FMT, bool VEC>
-__global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
+template <int FMT, bool VEC, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, int M, int N, int K, float alpha,
     const float* __restrict__ ga, const float* __restrict__ gb, float* __restrict__ C, int ldc) {
   using F = Fmt<FMT>;
+  using W = Waves<WM, WN>;
+  constexpr int kThreads = W::kThreads, FM = W::FM, FN = W::FN;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   if (ga) alpha = ga[0] * gb[0];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
   const int gm = (M + kBM - 1) / kBM, gn = (N + kBN - 1) / kBN;
   int tm, tn;
   tile_of(blockIdx.x, gm, gn, tm, tn);
@@ -123,59 +152,80 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
   const rsrc_t rBs = make_rsrc(Bs + (size_t)n0 * kgroups, (uint32_t)rowsB * kgroups);
   const int nst = (K + F::kStageK - 1) / F::kStageK;
 
-  // ---- global -> registers for one stage ----
-  // Thread t loads 16-B chunk (t & 7) of rows t/8 + 32 i (i = 0..7) of A and
-  // of B; a K chunk beyond the row end reads as zero through an OOB offset.
-  i32x4 rga[kLoads / 2], rgb[kLoads / 2];
-  uint32_t rsw[2][2];  // raw scale words of A row tid / B row tid (8 groups)
-  uint32_t rsb[2][8];  // byte-wise scale loads (K not a stage multiple)
-  const uint32_t lrow = (uint32_t)tid >> 3, lch = (uint32_t)tid & 7;
-  auto gload = [&](int st) {
-    const uint32_t kk = (uint32_t)st * kRowBytes + lch * 16;
-    const bool kin = kk < kbytes;
+  // ---- global -> LDS for one stage ----
+  // Codes go straight to LDS: wave w fills 1-KB blocks w*kBlocks .. +kBlocks-1
+  // (blocks 0..31 = A rows 8b..8b+7, 32..63 = B rows); lane l of a block
+  // writes slot l&7 of row 8b + l/8, i.e. global chunk (l&7) ^ ((row>>1)&7).
+  // Scale bytes go through registers and are rearranged after the MFMAs.
+  constexpr int kSR = (kBM + kBN) / kThreads;  // scale rows per thread (2 or 1)
+  uint32_t rsw[kSR][2];  // raw scale words of this thread's scale rows (8 groups)
+  uint32_t rsb[kSR][8];  // byte-wise scale loads (K not a stage multiple)
+  // Per-lane part of the load offsets: row 8b + l/8 of block b and the
+  // swizzled chunk, which depends only on the parity of b (rows 8b..8b+7
+  // have (row >> 1) & 7 = 4 (b & 1) + (l/8)/2).  The block part b*8*kbytes is
+  // wave-uniform.  Rows past the tile edge fall outside the buffer's range.
+  const uint32_t lrow8 = (uint32_t)lane >> 3;
+  const uint32_t c_even = ((uint32_t)lane & 7u) ^ ((lrow8 >> 1) & 7u);
+  const uint32_t c_odd = ((uint32_t)lane & 7u) ^ ((4u + (lrow8 >> 1)) & 7u);
+  const uint32_t vrow = lrow8 * kbytes;
+  // part p of NP issues this wave's code blocks p*kBlocks/NP .. (p+1)*kBlocks/NP-1
+  // (on = false: the loads are issued with out-of-range offsets and write
+  // zeros into the idle buffer; this keeps the substep free of branches)
+  auto gload_codes = [&](int st, int buf, int part, int nparts, bool on) {
+    uint8_t* base = lds + buf * kStageLds;
+    const uint32_t kb0 = (uint32_t)st * kRowBytes;
+    // lanes whose chunk lies past the row end (or all lanes when !on) get
+    // an out-of-range offset; done with masks so the code stays branch-free
+    const uint32_t all_off = on ? 0u : 0xFFFFFFFFu;
+    const int per = W::kBlocks / nparts;
 #pragma unroll
-    for (int i = 0; i < kLoads / 2; ++i) {
-      const uint32_t off = (lrow + 32u * i) * kbytes + kk;
-      rga[i] = buf_load16(rA, kin ? off : kOOB);
-      rgb[i] = buf_load16(rB, kin ? off : kOOB);
+    for (int q = 0; q < per; ++q) {
+      const int blk = wave * W::kBlocks + part * per + q;   // wave-uniform
+      const bool isA = blk < kBM / 8;
+      const uint32_t c = (blk & 1) ? c_odd : c_even;
+      const uint32_t kk = kb0 + c * 16;
+      uint32_t off = vrow + (uint32_t)((blk & (kBM / 8 - 1)) * 8) * kbytes + kk;
+      const uint32_t bad = all_off | (0u - (uint32_t)(kk >= kbytes));
+      off = (off & ~bad) | (kOOB & bad);
+      buf_load16_lds(isA ? rA : rB, base + blk * 1024, off);
     }
-    // raw scale words; they are only rearranged in sstore, after the MFMAs,
-    // so that no wait on this stage's loads happens before compute
-    const uint32_t g0 = (uint32_t)st * F::kGroups, base = (uint32_t)tid * kgroups + g0;
+  };
+  auto gload_scales = [&](int st, bool on) {
+    const uint32_t g0 = (uint32_t)st * F::kGroups;
+    const uint32_t all_off = on ? 0u : 0xFFFFFFFFu;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const rsrc_t rr = w == 0 ? rAs : rBs;
+    for (int w = 0; w < kSR; ++w) {
+      // scale row of this thread: A rows for w == 0 (kSR 2) or waves 0..3 (kSR 1)
+      const bool isA = kSR == 2 ? w == 0 : wave < 4;
+      const rsrc_t rr = isA ? rAs : rBs;
+      const uint32_t base_s =
+          (((uint32_t)(kSR == 2 ? tid : tid & 255) * kgroups + g0) & ~all_off) | (kOOB & all_off);
       if constexpr (VEC) {
         if constexpr (F::kGroups == 8) {
-          const i32x2 v = buf_load8(rr, base);
+          const i32x2 v = buf_load8(rr, base_s);
           rsw[w][0] = (uint32_t)v.x;
           rsw[w][1] = (uint32_t)v.y;
         } else {
-          rsw[w][0] = buf_load4(rr, base);
+          rsw[w][0] = buf_load4(rr, base_s);
           rsw[w][1] = 0;
         }
       } else {
         rsw[w][0] = rsw[w][1] = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const bool ok = j < F::kGroups && g0 + j < kgroups;
-          rsb[w][j] = buf_load1(rr, ok ? base + j : kOOB);
+          const bool ok = on && j < F::kGroups && g0 + j < kgroups;
+          rsb[w][j] = buf_load1(rr, ok ? base_s + j : kOOB);
         }
       }
     }
   };
   auto sstore = [&](int buf) {
     uint8_t* base = lds + buf * kStageLds;
-#pragma unroll
-    for (int i = 0; i < kLoads / 2; ++i) {
-      *reinterpret_cast<i32x4*>(base + (lrow + 32 * i) * kPitch + lch * 16) = rga[i];
-      *reinterpret_cast<i32x4*>(base + (kBM + lrow + 32 * i) * kPitch + lch * 16) = rgb[i];
-    }
     // dword h of a row holds groups h, 2+h, 4+h, 6+h: in K-substep s the
     // lanes of half h carry group 2s+h's scale (byte s, picked by op_sel)
     uint32_t* sp = reinterpret_cast<uint32_t*>(base + kCodeLds);
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
+    for (int w = 0; w < kSR; ++w) {
       uint32_t b[8];
       if constexpr (VEC) {
 #pragma unroll
@@ -187,72 +237,107 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) b[j] = rsb[w][j];
       }
-      const int row = w * kBM + tid;
+      const int row = kSR == 2 ? w * kBM + tid : tid;
       sp[row * 2] = b[0] | (b[2] << 8) | (b[4] << 16) | (b[6] << 24);
       sp[row * 2 + 1] = b[1] | (b[3] << 8) | (b[5] << 16) | (b[7] << 24);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int fr = lane & 31, fh = lane >> 5;
-  const int arow0 = wm * 128 + fr, brow0 = kBM + wn * 128 + fr;
+  const int arow0 = wm * (kBM / WM) + fr, brow0 = kBM + wn * (kBN / WN) + fr;
 
+  // fragment of row `row` (0..511 over A then B) for K-substep s:
+  // FP4: chunk 2s+h; FP8: chunks 4s+h and 4s+2+h
   auto frag = [&](const uint8_t* base, int row, int s) -> i32x8 {
-    const uint8_t* p = base + row * kPitch + s * F::kSubBytes + fh * 16;
-    const i32x4 v = *reinterpret_cast<const i32x4*>(p);
+    const int r = row & (kBM - 1);
+    const uint8_t* rb = base + (row >= kBM ? kBM * kRowBytes : 0);
     if constexpr (FMT == 4) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(rb + lds_slot(r, 2 * s + fh));
       return i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
     } else {
-      const i32x4 u = *reinterpret_cast<const i32x4*>(p + 32);
+      const i32x4 v = *reinterpret_cast<const i32x4*>(rb + lds_slot(r, 4 * s + fh));
+      const i32x4 u = *reinterpret_cast<const i32x4*>(rb + lds_slot(r, 4 * s + 2 + fh));
       return i32x8{v.x, v.y, v.z, v.w, u.x, u.y, u.z, u.w};
     }
   };
 
-  gload(0);
+  gload_codes(0, 0, 0, 1, true);
+  gload_scales(0, true);
   sstore(0);
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): stage 0 is in LDS
   __syncthreads();
 
   for (int st = 0; st < nst; ++st) {
     const uint8_t* base = lds + (st & 1) * kStageLds;
-    if (st + 1 < nst) gload(st + 1);
+    const bool more = st + 1 < nst;
+    // the last stage loads nothing (every offset is out of range) but keeps
+    // the loop body a single basic block
+    gload_scales(st + 1, more);
     const uint32_t* sb = reinterpret_cast<const uint32_t*>(base + kCodeLds);
-    uint32_t sca[4], scb[4];
+    uint32_t sca[FM], scb[FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sca[i] = sb[(arow0 + 32 * i) * 2 + fh];
-      scb[i] = sb[(brow0 + 32 * i) * 2 + fh];
-    }
-    i32x8 fa[2][4], fb[2][4];
+    for (int i = 0; i < FM; ++i) sca[i] = sb[(arow0 + 32 * i) * 2 + fh];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[0][i] = frag(base, arow0 + 32 * i, 0);
-      fb[0][i] = frag(base, brow0 + 32 * i, 0);
+    for (int j = 0; j < FN; ++j) scb[j] = sb[(brow0 + 32 * j) * 2 + fh];
+    // One wave per SIMD (4 waves): double-buffer the fragments so the next
+    // K-substep's LDS reads overlap this substep's MFMAs.  Two waves per SIMD
+    // (8 waves): single buffer; the sibling wave covers the LDS latency.
+    constexpr int NB = W::kMinWaves == 1 ? 2 : 1;
+    i32x8 fa[NB][FM], fb[NB][FN];
+    if constexpr (NB == 2) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[0][i] = frag(base, arow0 + 32 * i, 0);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[0][j] = frag(base, brow0 + 32 * j, 0);
     }
-    // substep S: prefetch S+1's fragments, then 16 MFMAs; op_sel S picks the
-    // scale byte of group 2S+h from each lane's scale dword
+    // substep S: the FM x FN MFMAs of S interleaved (in issue order) with the
+    // LDS reads of S+1's fragments and a share of the next stage's global
+    // loads, so that no more than a few LDS reads are outstanding when an
+    // MFMA is due; op_sel S picks the scale byte of group 2S+h.
     auto sub = [&](auto SC) {
       constexpr int S = decltype(SC)::value;
-      constexpr int cur = S & 1;
-      if constexpr (S + 1 < F::kSub) {
+      constexpr int cur = NB == 2 ? (S & 1) : 0;
+      constexpr int NP = F::kSub;  // global-load parts, one per substep
+      if constexpr (NB == 1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          fa[cur ^ 1][i] = frag(base, arow0 + 32 * i, S + 1);
-          fb[cur ^ 1][i] = frag(base, brow0 + 32 * i, S + 1);
-        }
+        for (int i = 0; i < FM; ++i) fa[0][i] = frag(base, arow0 + 32 * i, S);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[0][j] = frag(base, brow0 + 32 * j, S);
+      }
+      gload_codes(st + 1, (st + 1) & 1, S, NP, more);
+      if constexpr (NB == 2 && S + 1 < F::kSub) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[cur ^ 1][i] = frag(base, arow0 + 32 * i, S + 1);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[cur ^ 1][j] = frag(base, brow0 + 32 * j, S + 1);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               fa[cur][i], fb[cur][j], acc[i][j], FMT, FMT, S, (int)sca[i], S, (int)scb[j]);
+      if constexpr (NB == 2) {
+        // issue order: per group {MFMA, DS read, MFMA, VMEM, ...}
+        constexpr int nmf = FM * FN;
+        constexpr int nds = S + 1 < F::kSub ? (FM + FN) * (FMT == 4 ? 1 : 2) : 0;
+        constexpr int nvm = W::kBlocks / NP;
+#pragma unroll
+        for (int g = 0; g < nmf; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+          if (g < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+          if (g < nvm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     };
     sub(std::integral_constant<int, 0>{});
     sub(std::integral_constant<int, 1>{});
@@ -260,7 +345,11 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
       sub(std::integral_constant<int, 2>{});
       sub(std::integral_constant<int, 3>{});
     }
-    if (st + 1 < nst) sstore((st + 1) & 1);
+    sstore((st + 1) & 1);
+    // keep this stage's MFMAs above the wait: otherwise the scheduler sinks
+    // them below it and the next stage's loads stop overlapping the math
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);  // the next stage's LDS-direct loads have landed
     __syncthreads();
   }
 
@@ -268,39 +357,47 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
   const int rowsC = min(kBM, M - m0);
   const rsrc_t rC = make_rsrc(C + (size_t)m0 * ldc, (uint32_t)rowsC * (uint32_t)ldc * 4u);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + fr;
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn * (kBN / WN) + j * 32 + fr;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = wm * 128 + i * 32 + 8 * (v / 4) + 4 * fh + (v % 4);
-        const uint32_t off = col < N ? ((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 4u : kOOB;
+        const int row = wm * (kBM / WM) + i * 32 + 8 * (v / 4) + 4 * fh + (v % 4);
+        const uint32_t bad = 0u - (uint32_t)(col >= N);
+        const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 4u) & ~bad) | (kOOB & bad);
         buf_store4(alpha * acc[i][j][v], rC, off);
       }
     }
   }
 }
 
+template <int FMT, bool VEC, int WM, int WN>
+hipError_t gemm_launch_cfg(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                           int64_t m, int64_t n, int64_t k, float alpha, const float* ga,
+                           const float* gb, float* c, int64_t ldc, hipStream_t s) {
+  const size_t lds = 2 * (size_t)kStageLds;
+  const void* fn = reinterpret_cast<const void*>(&mx_gemm_kernel<FMT, VEC, WM, WN>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
+  hipLaunchKernelGGL((mx_gemm_kernel<FMT, VEC, WM, WN>), dim3((unsigned)tiles),
+                     dim3(Waves<WM, WN>::kThreads), lds, s, a, as, b, bs, (int)m, (int)n, (int)k,
+                     alpha, ga, gb, c, (int)ldc);
+  return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t gemm_launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                        int64_t m, int64_t n, int64_t k, float alpha, const float* ga,
                        const float* gb, float* c, int64_t ldc, hipStream_t s) {
-  const size_t lds = 2 * (size_t)kStageLds;
   // scale rows split into whole per-stage words when K is a stage multiple
   const bool vec = (k / 32) % Fmt<FMT>::kGroups == 0;
-  const void* fn = vec ? reinterpret_cast<const void*>(&mx_gemm_kernel<FMT, true>)
-                       : reinterpret_cast<const void*>(&mx_gemm_kernel<FMT, false>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
   if (vec)
-    hipLaunchKernelGGL((mx_gemm_kernel<FMT, true>), dim3((unsigned)tiles), dim3(kThreads), lds, s,
-                       a, as, b, bs, (int)m, (int)n, (int)k, alpha, ga, gb, c, (int)ldc);
-  else
-    hipLaunchKernelGGL((mx_gemm_kernel<FMT, false>), dim3((unsigned)tiles), dim3(kThreads), lds, s,
-                       a, as, b, bs, (int)m, (int)n, (int)k, alpha, ga, gb, c, (int)ldc);
-  return hipGetLastError();
+    return gemm_launch_cfg<FMT, true, FP4MX_GEMM_WM, FP4MX_GEMM_WN>(a, as, b, bs, m, n, k, alpha,
+                                                                  ga, gb, c, ldc, s);
+  return gemm_launch_cfg<FMT, false, FP4MX_GEMM_WM, FP4MX_GEMM_WN>(a, as, b, bs, m, n, k, alpha,
+                                                                 ga, gb, c, ldc, s);
 }
 
 }  // namespace

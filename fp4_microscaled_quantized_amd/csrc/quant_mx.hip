@@ -79,9 +79,15 @@ template <int ROUND>
 __device__ __forceinline__ void quant_group(const float (&y)[kGroup], uint32_t idx_lo,
                                             uint32_t kmix, uint32_t (&w)[4],
                                             uint32_t& scale) {
-  uint32_t m = 0;
+  // group max |y| with NaN propagation (IEEE maximum): non-finite iff the
+  // result's magnitude bits reach the Inf pattern
+  float am = __builtin_elementwise_maximum(__builtin_fabsf(y[30]), __builtin_fabsf(y[31]));
 #pragma unroll
-  for (int i = 0; i < kGroup; ++i) m = max(m, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+  for (int i = 0; i < 30; i += 3)
+    am = __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(am, __builtin_fabsf(y[i])),
+        __builtin_elementwise_maximum(__builtin_fabsf(y[i + 1]), __builtin_fabsf(y[i + 2])));
+  const uint32_t m = __float_as_uint(am) & 0x7FFFFFFFu;
   if (m >= 0x7F800000u) {  // Inf or NaN in the group
 #pragma unroll
     for (int k = 0; k < 4; ++k) w[k] = 0;
@@ -91,17 +97,17 @@ __device__ __forceinline__ void quant_group(const float (&y)[kGroup], uint32_t i
   const int code = max((int)(m >> 23) - 2, 0);
   scale = (uint32_t)code;
   if constexpr (ROUND == FP4MX_ROUND_RTN) {
-    // RNE(y * 2^(127-code)) == RNE(y / X) with X = 2^(code-127).  X = 2^-127
-    // (code 0) is subnormal in fp32; that case uses (y*2^64) / 2^-63 instead.
-    const float pre = code == 0 ? 0x1p64f : 1.0f;
-    const float X = code == 0 ? 0x1p-63f : __uint_as_float((uint32_t)code << 23);
+    // v_cvt_scalef32_pk_fp4_f32 computes E2M1 RNE (saturating) of y / X with
+    // X = 2^(code-127); code 0 passes the subnormal fp32 2^-127, which the
+    // converter takes as that power of two.
+    const float X = __uint_as_float(code == 0 ? 0x00400000u : (uint32_t)code << 23);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t r = 0;
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * k + 0] * pre, y[8 * k + 1] * pre, X, 0);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * k + 2] * pre, y[8 * k + 3] * pre, X, 1);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * k + 4] * pre, y[8 * k + 5] * pre, X, 2);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * k + 6] * pre, y[8 * k + 7] * pre, X, 3);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * k + 0], y[8 * k + 1], X, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * k + 2], y[8 * k + 3], X, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * k + 4], y[8 * k + 5], X, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * k + 6], y[8 * k + 7], X, 3);
       w[k] = r;
     }
   } else {
@@ -115,22 +121,18 @@ __device__ __forceinline__ void quant_group(const float (&y)[kGroup], uint32_t i
         const int i = 8 * k + j;
         const float v = __builtin_fabsf(y[i]) * f;  // 0 <= v < 6
         const uint32_t vb = __float_as_uint(v);
-        const uint32_t ev = vb >> 23;
-        float a, sc;
-        uint32_t qa;
-        if (ev >= 127u) {  // v in [1, 6): grid steps 0.5, 1, 2
-          a = __uint_as_float(vb & 0xFFC00000u);
-          qa = (vb >> 22) - 252u;
-          sc = __uint_as_float((279u - ev) << 23);  // 2^24 / gap
-        } else {           // v in [0, 1): grid step 0.5
-          a = ev == 126u ? 0.5f : 0.0f;
-          qa = ev == 126u ? 1u : 0u;
-          sc = 0x1p25f;
-        }
-        const float P = (v - a) * sc;  // probability * 2^24, exact
         const uint32_t r = fmix32((idx_lo + (uint32_t)i) ^ kmix);
-        const float u = (float)(r >> 8);
-        uint32_t q = qa + (u < P ? 1u : 0u);
+        // round up iff (r >> 8) * 2^-24 < (v - a) / (b - a):
+        //  v in [1, 6):   (v-a)/(b-a) = frac22 / 2^22  ->  (r >> 10) < frac22
+        //  v in [0.5, 1): (v-a)/(b-a) = frac23 / 2^23  ->  (r >> 9)  < frac23
+        //  v < 0.5:       (v-a)/(b-a) = 2v             ->  (r >> 8) < v * 2^25
+        const bool hi = vb >= 0x3F800000u;
+        const uint32_t lim = vb & (hi ? 0x3FFFFFu : 0x7FFFFFu);
+        const uint32_t rr = r >> (hi ? 10 : 9);
+        const uint32_t base = hi ? (vb >> 22) - 252u : 1u;
+        const uint32_t qa = base + (rr < lim ? 1u : 0u);
+        const uint32_t qb = (float)(r >> 8) < v * 0x1p25f ? 1u : 0u;
+        uint32_t q = vb >= 0x3F000000u ? qa : qb;
         q |= (__float_as_uint(y[i]) >> 28) & 8u;
         word |= q << (4 * j);
       }
@@ -143,23 +145,66 @@ __device__ __forceinline__ uint32_t group_kmix(uint64_t idx0, uint32_t key_lo, u
   return key_lo ^ fmix32((uint32_t)(idx0 >> 32) ^ key_hi);
 }
 
+// 32-bit unsigned division by a launch constant: q = (umulhi(n, mul) + n) >> sh
+// (Granlund-Montgomery), exact for n < 2^31.
+struct FastDiv {
+  uint32_t mul, sh, d;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t sh = 0;
+  while ((1ull << sh) < d) ++sh;
+  const uint64_t mul = ((1ull << 32) * ((1ull << sh) - d)) / d + 1;
+  return FastDiv{(uint32_t)mul, sh, d};
+}
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.mul) + n) >> f.sh;
+}
+
 // ---------------------------------------------------------------------------
-// Row axis, direct from HBM: thread = one group of one row.
+// Row axis: thread = one group of one row.  Each wave stages its 64 groups
+// (4 KB of bf16) through LDS so the global reads are fully coalesced 16-B
+// loads (lane l reads bytes 16 l + 1024 q), then each lane reads back its own
+// 64-byte group.  Groups are numbered row-major over (row, group-in-row).
 // ---------------------------------------------------------------------------
+constexpr int kWaveStage = 64 * 64 + 16 * 4;  // 64 groups of 64 B, 16-B pad per 16 groups
+
 template <bool HAD, int ROUND>
 __global__ __launch_bounds__(256) void quant_row_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
     uint32_t key_lo, uint32_t key_hi, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales) {
-  const int64_t gpr = cols / kGroup;
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= rows * gpr) return;
-  const int64_t row = g / gpr, grp = g - row * gpr;
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ld + grp * kGroup);
+    uint8_t* __restrict__ scales, FastDiv gdiv, uint32_t ngroups) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4 * kWaveStage];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint8_t* ws = stage + wave * kWaveStage;
+  const uint32_t g_wave = blockIdx.x * 256u + (uint32_t)wave * 64u;  // first group of the wave
+  if (g_wave >= ngroups) return;
+  // cooperative coalesced load: chunk q*64 + lane (16 B) of the wave's 64 groups
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t chunk = (uint32_t)q * 64u + (uint32_t)lane;  // 0..255
+    const uint32_t g = g_wave + chunk / 4u;
+    if (g < ngroups) {
+      const uint32_t row32 = fastdiv(g, gdiv);
+      const int64_t grp = g - row32 * gdiv.d;
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          x + (int64_t)row32 * ld + grp * kGroup + (chunk & 3u) * 8));
+      *reinterpret_cast<u32x4*>(ws + chunk * 16 + (chunk / 64u) * 16) = v;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+  const uint32_t g = g_wave + (uint32_t)lane;
+  if (g >= ngroups) return;
+  const uint32_t row32 = fastdiv(g, gdiv);
+  const int64_t row = row32, grp = g - row32 * gdiv.d;
+  const int64_t gpr = gdiv.d;
   uint32_t wd[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const u32x4 v = __builtin_nontemporal_load(src + q);
+    const uint32_t chunk = (uint32_t)lane * 4u + (uint32_t)q;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ws + chunk * 16 + (chunk / 64u) * 16);
     wd[4 * q + 0] = v.x; wd[4 * q + 1] = v.y; wd[4 * q + 2] = v.z; wd[4 * q + 3] = v.w;
   }
   float t[kGroup];
@@ -292,21 +337,24 @@ hipError_t tile_dispatch(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
 hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                             bool hadamard, const QuantOut& o, hipStream_t s) {
   const int64_t groups = rows * (cols / kGroup);
+  if (groups >= (1ll << 31)) return launch_quant_tile(x, rows, cols, ld, hadamard, &o, nullptr, s);
+  const FastDiv gd = make_fastdiv((uint32_t)(cols / kGroup));
   const unsigned nblk = (unsigned)((groups + 255) / 256);
+  const uint32_t ng = (uint32_t)groups;
   if (hadamard) {
     if (o.rounding == FP4MX_ROUND_RTN)
       hipLaunchKernelGGL((quant_row_kernel<true, 0>), dim3(nblk), dim3(256), 0, s, x, rows, cols,
-                         ld, o.sign_mask, o.key.lo, o.key.hi, o.codes, o.scales);
+                         ld, o.sign_mask, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng);
     else
       hipLaunchKernelGGL((quant_row_kernel<true, 1>), dim3(nblk), dim3(256), 0, s, x, rows, cols,
-                         ld, o.sign_mask, o.key.lo, o.key.hi, o.codes, o.scales);
+                         ld, o.sign_mask, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng);
   } else {
     if (o.rounding == FP4MX_ROUND_RTN)
       hipLaunchKernelGGL((quant_row_kernel<false, 0>), dim3(nblk), dim3(256), 0, s, x, rows, cols,
-                         ld, 0u, o.key.lo, o.key.hi, o.codes, o.scales);
+                         ld, 0u, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng);
     else
       hipLaunchKernelGGL((quant_row_kernel<false, 1>), dim3(nblk), dim3(256), 0, s, x, rows, cols,
-                         ld, 0u, o.key.lo, o.key.hi, o.codes, o.scales);
+                         ld, 0u, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng);
   }
   return hipGetLastError();
 }
