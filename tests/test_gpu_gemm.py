@@ -25,7 +25,9 @@ def _to_dev_mx(codes, scales):
 
 
 @pytest.mark.parametrize("m,n,k", [(64, 128, 128), (32, 32, 32), (96, 160, 320), (128, 128, 256),
-                                   (256, 384, 1024), (160, 96, 288), (512, 256, 2048)])
+                                   (256, 384, 1024), (160, 96, 288), (512, 256, 2048),
+                                   (288, 224, 384), (544, 480, 1152), (768, 512, 640),
+                                   (544, 480, 2048), (96, 800, 3072)])
 def test_gemm_parity(m, n, k):
     log("gemm", m, n, k)
     a, b = _operands(m, n, k)
