@@ -5,8 +5,10 @@ One step = one pass of the whole hot path over one batch of synthetic input:
 forward (RHT + RTN quantization of X and W fused with the SR context, FP4
 GEMM Y = X W^T) and backward (RHT + SR quantization of dY and dY^T, FP4 GEMMs
 dX and dW), i.e. the kernels fp4mx_linear_fwd + fp4mx_linear_bwd launch,
-called here one by one through the C ABI so that each launch is bracketed by
-HIP events on the stream it runs on.
+called here one by one through the C ABI.  The timed steps run back to back
+with HIP events at step boundaries only (value, ms_per_step); the same number
+of steps is then run again with an event after every launch, which gives each
+kernel's in-step duration (breakdown_ms and the roofline).
 
 Headline workload: Quartet-style layer, 8192 tokens, d_in = d_out = 4096.
 value = 6*M*N*K flop / step time (TFLOP/s).  Printed as one JSON line.
@@ -56,7 +58,7 @@ def dev_bf16(bits):
 
 
 class LinearStep:
-    """The MXFP4 linear fwd+bwd hot path through the C ABI, with per-launch events."""
+    """The MXFP4 linear fwd+bwd hot path as six C-ABI launches on one stream."""
 
     def __init__(self, d, seed=0):
         import torch
@@ -104,23 +106,35 @@ class LinearStep:
         ]
 
     def run(self, steps, timed):
+        """`steps` passes of the six launches, back to back; when timed, one
+        event per step boundary (no events between the kernels of a step)."""
+        import torch
+        calls = self._calls()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)] if timed else None
+        if timed:
+            evs[0].record()
+        for i in range(steps):
+            for c in calls:
+                c()
+            if timed:
+                evs[i + 1].record()
+        return evs
+
+    def kernel_times(self, steps):
+        """In-step duration of each launch: the same steps again with an event
+        after every launch, all on the stream the kernels run on (an event
+        record adds a few microseconds to the launch it follows)."""
         import torch
         calls = self._calls()
         evs = []
         for _ in range(steps):
-            if timed:
-                ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-                ev[0].record()
-                for i, c in enumerate(calls):
-                    c()
-                    ev[i + 1].record()
-                evs.append(ev)
-            else:
-                for c in calls:
-                    c()
-        return evs
-
-    def collect(self, evs):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+            ev[0].record()
+            for i, c in enumerate(calls):
+                c()
+                ev[i + 1].record()
+            evs.append(ev)
+        torch.cuda.synchronize()
         for ev in evs:
             for i, nm in enumerate(self.names):
                 self.times[nm].append(ev[i].elapsed_time(ev[i + 1]))
@@ -152,9 +166,31 @@ def time_linear(d, steps, warmup, seed=0):
     evs = st.run(steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    st.collect(evs)
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    st.kernel_times(steps)
     avg = {nm: float(np.mean(v)) for nm, v in st.times.items()}
-    return st, wall, avg
+    return st, wall, avg, step_ms
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "mx_gemm_kernel_quartet_8192x4096x4096_traffic.json")
+
+
+def gemm_traffic(st):
+    """Mean HBM bytes per GEMM launch from the committed FETCH_SIZE / WRITE_SIZE
+    record (copy-calibrated), if it was taken on this exact kernel source and
+    workload; None otherwise."""
+    import hashlib
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError, KeyError):
+        return None
+    if sha != rec["source_sha256"] or "%dx%dx%d" % (st.m, st.n, st.k) != rec["workload"]:
+        return None
+    b = rec["bytes_per_launch"]
+    return int(round(np.mean([b["gemm_y"], b["gemm_dx"], b["gemm_dw"]])))
 
 
 def gemm_roofline(st, avg):
@@ -166,7 +202,11 @@ def gemm_roofline(st, avg):
     achieved = tot_fl / (tot_ms * 1e-3) / 1e12
     return {"bound": "mfma", "kernel": "mx_gemm_kernel (FP4 32x32x64 scaled MFMA)",
             "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": gemm_traffic(st),
+            "traffic_unit": "bytes per launch (HBM/fabric, FETCH_SIZE + WRITE_SIZE)",
+            "algorithmic_bytes_per_launch": int(round(np.mean(
+                [(m + n) * k * 17 // 32 + 4 * m * n, (m + k) * n * 17 // 32 + 4 * m * k,
+                 (n + k) * m * 17 // 32 + 4 * n * k]))),
             "per_launch_ms": {x: round(avg[x], 4) for x in fl}}
 
 
@@ -290,7 +330,7 @@ def main():
     else:
         d = synth.llama_ffn_up(0)
         wl = {"workload": "llama3_8b_ffn_up fwd+bwd M=8192 K=4096 N=14336", "m": 8192, "n": 14336, "k": 4096}
-    st, wall, avg = time_linear(d, a.steps, a.warmup)
+    st, wall, avg, step_ms = time_linear(d, a.steps, a.warmup)
     ev_ms = sum(avg.values())
     ms_step = wall * 1e3 / a.steps
     value = st.flops() / (ms_step * 1e-3) / 1e12
@@ -302,14 +342,15 @@ def main():
         "frac_fp4_peak": round(value / PEAK_FP4_TFLOPS, 4),
         "roofline": gemm_roofline(st, avg),
         "breakdown_ms": {k2: round(v, 4) for k2, v in avg.items()},
-        "event_sum_ms_per_step": round(ev_ms, 4),
+        "kernel_sum_ms_per_step": round(ev_ms, 4),
+        "event_ms_per_step": round(float(np.mean(step_ms)), 4),
         "quantizer_roofline_in_step": quant_roofline(st, avg),
     }
     del st
     torch.cuda.empty_cache()
     if not a.no_extra:
         if a.workload == "quartet":
-            st2, wall2, avg2 = time_linear(synth.llama_ffn_up(0), a.steps, a.warmup)
+            st2, wall2, avg2, _ = time_linear(synth.llama_ffn_up(0), a.steps, a.warmup)
             ms2 = wall2 * 1e3 / a.steps
             out["llama_ffn_up"] = {"workload": "8192 x 4096 -> 14336 fwd+bwd", "ms_per_step": round(ms2, 4),
                                    "TFLOP/s": round(st2.flops() / (ms2 * 1e-3) / 1e12, 1),
