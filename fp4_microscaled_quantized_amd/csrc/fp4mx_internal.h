@@ -29,6 +29,23 @@ inline RngKey make_key(uint64_t seed, uint32_t stream) {
   return RngKey{(uint32_t)k, (uint32_t)(k >> 32)};
 }
 
+// 32-bit unsigned division by a launch constant: q = (umulhi(n, mul) + n) >> sh
+// (Granlund-Montgomery round-up method), exact for n < 2^31.
+struct FastDiv {
+  uint32_t mul, sh, d;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t sh = 0;
+  while ((1ull << sh) < d) ++sh;
+  const uint64_t mul = ((1ull << 32) * ((1ull << sh) - d)) / d + 1;
+  return FastDiv{(uint32_t)mul, sh, d};
+}
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.mul) + n) >> f.sh;
+}
+
 // Quantizer launch description for one output operand.
 struct QuantOut {
   int rounding;        // FP4MX_ROUND_RTN / FP4MX_ROUND_SR

@@ -145,23 +145,6 @@ __device__ __forceinline__ uint32_t group_kmix(uint64_t idx0, uint32_t key_lo, u
   return key_lo ^ fmix32((uint32_t)(idx0 >> 32) ^ key_hi);
 }
 
-// 32-bit unsigned division by a launch constant: q = (umulhi(n, mul) + n) >> sh
-// (Granlund-Montgomery), exact for n < 2^31.
-struct FastDiv {
-  uint32_t mul, sh, d;
-};
-
-inline FastDiv make_fastdiv(uint32_t d) {
-  uint32_t sh = 0;
-  while ((1ull << sh) < d) ++sh;
-  const uint64_t mul = ((1ull << 32) * ((1ull << sh) - d)) / d + 1;
-  return FastDiv{(uint32_t)mul, sh, d};
-}
-
-__device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
-  return (__umulhi(n, f.mul) + n) >> f.sh;
-}
-
 // ---------------------------------------------------------------------------
 // Row axis: thread = one group of one row.  Each wave stages its 64 groups
 // (4 KB of bf16) through LDS so the global reads are fully coalesced 16-B
