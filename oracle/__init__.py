@@ -21,9 +21,11 @@ open the reading taken is stated in the function's docstring.
 Pinned: codecs (exhaustive / library routes), the FWHT (Sylvester matrix,
 orthogonality), the RNG (published test vectors), SR (exact probabilities,
 unbiasedness), GEMM (brute-force triple loop), linear backward (expectation
-equals the exact gradient), NVFP4 RTN and RTN+4/6 (the pages' Table 1 MSEs).
+equals the exact gradient), NVFP4 RTN and RTN+4/6 (the pages' Table 1 MSEs),
+MS-EDEN and the NVFP4 SR baseline (Table 1 MSEs, the EDEN correction range,
+RHT_128 structure, unbiasedness of the scale rounding and of the product).
 Parity unpinned: the FP8 staging of the NVFP4 GEMM (a design of this library
 that the pages do not describe; only its self-consistency is checked).
 """
 
-from . import formats, rng, rht, mx, nvfp4  # noqa: F401
+from . import formats, rng, rht, mx, nvfp4, msedn  # noqa: F401

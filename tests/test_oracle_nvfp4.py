@@ -12,7 +12,7 @@ def test_table1_rtn_and_four_over_six(golden):
         d = nvfp4.dequantize(*nvfp4.quantize46(x, use46))
         got[name] = np.mean((d - x) ** 2) * 1e3
     # the page prints one decimal: hold to +-0.3e-3
-    for k in want:
+    for k in got:
         assert abs(got[k] - want[k]) < 0.3, (k, got[k], want[k])
     assert got["rtn_46"] < got["rtn"]
 
