@@ -33,9 +33,12 @@ Readings taken (the pages leave these open):
       bits (nearest, ties to even) on its encoding, exponent unbounded;
     - q_i = E2M1_RNE_sat(fl(y_i / p)) (q = sign only when p = 0);
     - r_i = val(q_i) * p (exact);
-    - S = fl(num / den) per 128-chunk with num = sum fl(y_i^2), den =
-      sum fl(y_i r_i), both pairwise fp32 trees in index order (S = 1 if
-      den <= 0);
+    - S = fl(num / den) per 128-chunk with num = sum fl(z_i^2), den =
+      sum fl(z_i t_i), z = fl(y * 2^-E), t = fl(r * 2^-E), 2^E <= max|y| <
+      2^(E+1) over the chunk (E = 0 for a zero chunk), both pairwise fp32
+      trees in index order (S = 1 if den <= 0).  The power-of-two scaling
+      leaves S unchanged mathematically and keeps the squares finite for any
+      finite input;
     - v_g = fl(S * p_g); m = max over the tensor of v_g; tensor scale 2^k with
       k the least integer such that m * 2^-k <= 256 (k = 0 when m = 0);
     - group scale = SR_E4M3(fl32(v_g * 2^-k)) with u = (r >> 8) * 2^-24 from
@@ -167,12 +170,24 @@ def msedn_pass1(y: np.ndarray, s: float = 6.0):
     r = (formats.e2m1_decode(q).astype(np.float32) * pe).astype(np.float32)
     yc = y.reshape(R, C // CHUNK, CHUNK)
     rc = r.reshape(R, C // CHUNK, CHUNK)
-    num = _pairwise((yc * yc).astype(np.float32))
-    den = _pairwise((yc * rc).astype(np.float32))
+    # S is invariant under scaling the chunk by a power of two: the sums are
+    # taken on y * 2^-E, r * 2^-E with 2^E <= max|y| < 2^(E+1), so no square
+    # overflows (exact scaling whenever nothing under- or overflows)
+    E = chunk_exponent(np.max(np.abs(yc), axis=-1))
+    ys = np.ldexp(yc, -E[..., None]).astype(np.float32)
+    rsc = np.ldexp(rc, -E[..., None]).astype(np.float32)
+    num = _pairwise((ys * ys).astype(np.float32))
+    den = _pairwise((ys * rsc).astype(np.float32))
     with np.errstate(divide="ignore", invalid="ignore"):
         S = np.where(den > 0, (num / np.where(den > 0, den, 1)).astype(np.float32), np.float32(1.0))
     vS = (np.repeat(S, CHUNK // GROUP, axis=-1) * p).astype(np.float32)
     return q.reshape(R, C), vS, S.astype(np.float32), p
+
+
+def chunk_exponent(m: np.ndarray) -> np.ndarray:
+    """floor(log2 m) for m > 0 (fp32 subnormals included), 0 for m = 0."""
+    f, e = np.frexp(np.asarray(m, dtype=np.float64))
+    return np.where(np.asarray(m) > 0, e - 1, 0).astype(np.int64)
 
 
 def range_exponent(m: float) -> int:

@@ -171,3 +171,17 @@ def test_zero_rows_and_chunks():
     mag = formats.e2m1_decode(np.stack([codes & 7, codes >> 4 & 7], -1))    # rotated zeros may be -0
     assert np.all(mag[0] == 0) and np.all(sc[0] == 0) and np.all(S[0] == 1.0)
     assert np.all(mag[1, :64] == 0) and S[1, 0] == 1.0 and 0.9 < S[1, 1] < 1.1
+
+
+def test_eden_s_scale_invariant_and_finite_for_huge_inputs():
+    """S is taken on the power-of-two-scaled chunk: the same for x and
+    2^j x, and finite when squares of the raw values would overflow fp32."""
+    x = np.random.default_rng(14).standard_normal((4, 256)).astype(np.float32)
+    w = msedn.sign_mask128(0, 0)
+    S0 = msedn.msedn_pass1(msedn.rht128(x, w))[2]
+    for j in (-100, 60, 100):
+        Sj = msedn.msedn_pass1(msedn.rht128(np.ldexp(x, j).astype(np.float32), w))[2]
+        assert np.array_equal(S0, Sj), j
+    x[0, 3] = 1e30
+    q, vS, S, p = msedn.msedn_pass1(msedn.rht128(x, w))
+    assert np.all(np.isfinite(S)) and np.all(np.isfinite(vS))
