@@ -52,6 +52,11 @@ _SIGS = {
     "fp4nv_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4nv_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4nv_linear_fwd": (_INT, [_P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "fp4nv_msedn_workspace_bytes": (_SZ, [_I64, _I64]),
+    "fp4nv_msedn_quantize": (_INT, [_P, _I64, _I64, _I64, _INT, C.c_float, _U64, _U32, _U32, _P, _P,
+                                    _P, _P, _P, _SZ, _P]),
+    "fp4nv_linear_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "fp4nv_linear_bwd": (_INT, [_P, _P, _P, _I64, _I64, _I64, _U64, _P, _P, _P, _SZ, _P]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -252,6 +257,37 @@ def nv_linear_fwd(x, w, ws=None, out=None):
     _check(lib().fp4nv_linear_fwd(_ptr(x), _ptr(w), m, n, k, _ptr(y), _ptr(ws), ws.numel(),
                                   _stream(dev)))
     return y
+
+
+def nv_msedn_quantize(x, axis=ROW, seed=0, gemm_id=1, stream=5, clip=6.0, want_s=False):
+    """MS-EDEN of x (bf16 2-D): NVTensor of the output operand ([rows, cols]
+    for ROW, [cols, rows] for COL), plus S per 128-chunk when want_s."""
+    R, Cc, ld = _bf16_2d(x)
+    dev = x.device
+    orow, ocol = (R, Cc) if axis == ROW else (Cc, R)
+    out = NVTensor(torch.empty((orow, ocol // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((orow, ocol // 16), dtype=torch.uint8, device=dev),
+                   torch.empty(1, dtype=torch.float32, device=dev))
+    s_out = torch.empty((orow, ocol // 128), dtype=torch.float32, device=dev) if want_s else None
+    ws = torch.empty(lib().fp4nv_msedn_workspace_bytes(R, Cc), dtype=torch.uint8, device=dev)
+    _check(lib().fp4nv_msedn_quantize(_ptr(x), R, Cc, ld, axis, float(clip), int(seed), gemm_id, stream,
+                                      _ptr(out.codes), _ptr(out.scales), _ptr(out.tensor_scale),
+                                      _ptr(s_out) if want_s else None, _ptr(ws), ws.numel(), _stream(dev)))
+    return (out, s_out) if want_s else out
+
+
+def nv_linear_bwd(dy, x, w, seed=0, ws=None, dx=None, dw=None):
+    """NVFP4 backward with MS-EDEN operands: (dX [m,k], dW [n,k]) fp32."""
+    m, n, _ = _bf16_2d(dy)
+    _, k, _ = _bf16_2d(x)
+    dev = dy.device
+    if ws is None:
+        ws = torch.empty(lib().fp4nv_linear_bwd_workspace_bytes(m, n, k), dtype=torch.uint8, device=dev)
+    dx = dx if dx is not None else torch.empty((m, k), dtype=torch.float32, device=dev)
+    dw = dw if dw is not None else torch.empty((n, k), dtype=torch.float32, device=dev)
+    _check(lib().fp4nv_linear_bwd(_ptr(dy), _ptr(x), _ptr(w), m, n, k, int(seed), _ptr(dx), _ptr(dw),
+                                  _ptr(ws), ws.numel(), _stream(dev)))
+    return dx, dw
 
 
 # --------------------------- autograd wrapper --------------------------------

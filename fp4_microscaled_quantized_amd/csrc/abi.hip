@@ -2,6 +2,8 @@
 // carving and kernel dispatch.  Every declaration, its source passage, and the
 // argument contract are in include/fp4mx.h.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -338,6 +340,107 @@ int fp4nv_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t
   if (e == hipSuccess) e = launch_nv_quant(wb, n, k, k, 1, amax_w, wq, wsc, gw, s);
   if (e != hipSuccess) return hip_fail(e);
   return nv_gemm_impl(xq, xs, gx, wq, wsc, gw, m, n, k, y, n, cv.p, s);
+}
+
+size_t fp4nv_msedn_workspace_bytes(int64_t rows, int64_t cols) {
+  if (!dim_ok(rows) || !dim_ok(cols)) return 0;
+  return round_up((size_t)rows * cols / 16 * sizeof(float)) + 256;
+}
+
+static int msedn_impl(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                      float clip_s, uint64_t seed, uint32_t gemm_id, uint32_t stream,
+                      uint8_t* codes, uint8_t* scales, float* ts, float* eden_s, uint8_t* ws,
+                      hipStream_t s) {
+  Carver cv{ws};
+  float* vbuf = reinterpret_cast<float*>(cv.take((size_t)rows * cols / 16 * sizeof(float)));
+  uint32_t* gmax = reinterpret_cast<uint32_t*>(cv.take(4));
+  hipError_t e = launch_msedn(static_cast<const uint16_t*>(x), rows, cols, ld, axis, clip_s, seed,
+                              gemm_id, stream, codes, scales, ts, eden_s, vbuf, gmax, s);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+int fp4nv_msedn_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                         float clip_s, uint64_t seed, uint32_t gemm_id, uint32_t rng_stream,
+                         uint8_t* codes, uint8_t* scales, float* tensor_scale, float* eden_s,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !codes || !scales || !tensor_scale) return FP4MX_E_NULL;
+  if (!dim_ok(rows) || !dim_ok(cols) || ld < cols) return FP4MX_E_SHAPE;
+  if (axis != FP4MX_AXIS_ROW && axis != FP4MX_AXIS_COL) return FP4MX_E_ARG;
+  if ((axis == FP4MX_AXIS_ROW ? cols : rows) % 128 != 0) return FP4MX_E_SHAPE;
+  if (!(clip_s > 0.0f) || !(clip_s < 1e30f)) return FP4MX_E_ARG;
+  if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scales & 1u) || ld % 8 != 0 ||
+      ((uintptr_t)tensor_scale & 3u) || ((uintptr_t)eden_s & 3u))
+    return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4nv_msedn_workspace_bytes(rows, cols)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  return msedn_impl(x, rows, cols, ld, axis, clip_s, seed, gemm_id, rng_stream, codes, scales,
+                    tensor_scale, eden_s, static_cast<uint8_t*>(ws), (hipStream_t)stream);
+}
+
+size_t fp4nv_linear_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
+  // two quantized operands per GEMM (live at once), the larger MS-EDEN
+  // scratch and the larger FP8 staging; operands of the two GEMMs are reused
+  const size_t q1 = nv_operand_bytes(m, n) + nv_operand_bytes(k, n);
+  const size_t q2 = nv_operand_bytes(n, m) + nv_operand_bytes(k, m);
+  const size_t ms = std::max(fp4nv_msedn_workspace_bytes(m, n), std::max(fp4nv_msedn_workspace_bytes(n, k),
+                                                                        fp4nv_msedn_workspace_bytes(m, k)));
+  const size_t gs = std::max(fp4nv_gemm_workspace_bytes(m, k, n), fp4nv_gemm_workspace_bytes(n, k, m));
+  return std::max(q1, q2) + ms + gs + 512;
+}
+
+int fp4nv_linear_bwd(const void* dy, const void* x, const void* w, int64_t m, int64_t n, int64_t k,
+                     uint64_t seed, float* dx, float* dw, void* ws, size_t ws_bytes, void* stream) {
+  if (!dy || !x || !w || !dx || !dw) return FP4MX_E_NULL;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k) || m % 128 != 0 || n % 128 != 0) return FP4MX_E_SHAPE;
+  if (!aligned16(dy) || !aligned16(x) || !aligned16(w) || !aligned16(dx) || !aligned16(dw))
+    return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4nv_linear_bwd_workspace_bytes(m, n, k)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const float clip = 6.0f;
+  const size_t qmax = std::max(nv_operand_bytes(m, n) + nv_operand_bytes(k, n),
+                               nv_operand_bytes(n, m) + nv_operand_bytes(k, m));
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* ms = base + qmax;
+  uint8_t* gws = ms + std::max(fp4nv_msedn_workspace_bytes(m, n),
+                               std::max(fp4nv_msedn_workspace_bytes(n, k), fp4nv_msedn_workspace_bytes(m, k)));
+  const uint16_t* dyb = static_cast<const uint16_t*>(dy);
+  // dX = dY W: inner dimension n
+  {
+    Carver cv{base};
+    uint8_t* aq = cv.take((size_t)m * n / 2);
+    uint8_t* as = cv.take((size_t)m * n / 16);
+    float* ag = reinterpret_cast<float*>(cv.take(256));
+    uint8_t* bq = cv.take((size_t)k * n / 2);
+    uint8_t* bs = cv.take((size_t)k * n / 16);
+    float* bg = reinterpret_cast<float*>(cv.take(256));
+    if ((st = msedn_impl(dy, m, n, n, FP4MX_AXIS_ROW, clip, seed, 1, 5, aq, as, ag, nullptr, ms, s)))
+      return st;
+    if ((st = msedn_impl(w, n, k, k, FP4MX_AXIS_COL, clip, seed, 1, 6, bq, bs, bg, nullptr, ms, s)))
+      return st;
+    if ((st = nv_gemm_impl(aq, as, ag, bq, bs, bg, m, k, n, dx, k, gws, s))) return st;
+  }
+  // dW = dY^T X: inner dimension m
+  {
+    Carver cv{base};
+    uint8_t* aq = cv.take((size_t)n * m / 2);
+    uint8_t* as = cv.take((size_t)n * m / 16);
+    float* ag = reinterpret_cast<float*>(cv.take(256));
+    uint8_t* bq = cv.take((size_t)k * m / 2);
+    uint8_t* bs = cv.take((size_t)k * m / 16);
+    float* bg = reinterpret_cast<float*>(cv.take(256));
+    if ((st = msedn_impl(dyb, m, n, n, FP4MX_AXIS_COL, clip, seed, 2, 7, aq, as, ag, nullptr, ms, s)))
+      return st;
+    if ((st = msedn_impl(x, m, k, k, FP4MX_AXIS_COL, clip, seed, 2, 8, bq, bs, bg, nullptr, ms, s)))
+      return st;
+    if ((st = nv_gemm_impl(aq, as, ag, bq, bs, bg, n, k, m, dw, k, gws, s))) return st;
+  }
+  return FP4MX_OK;
 }
 
 }  // extern "C"

@@ -66,6 +66,14 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                           const uint8_t* bs, int64_t m, int64_t n, int64_t k, float alpha,
                           float* c, int64_t ldc, hipStream_t s);
 
+// MS-EDEN, two passes (csrc/msedn.hip).  vbuf: fp32 per output 16-group;
+// gmax: one uint32 (global max of vbuf).
+hipError_t launch_msedn(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                        float clip_s, uint64_t seed, uint32_t gemm_id, uint32_t stream,
+                        uint8_t* codes, uint8_t* scales, float* tensor_scale, float* eden_s,
+                        float* vbuf, uint32_t* gmax, hipStream_t s);
+void msedn_sign_words(uint64_t seed, uint32_t gemm_id, uint32_t (&w)[4]);
+
 hipError_t launch_nv_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                           uint32_t* amax_bits, hipStream_t s);
 hipError_t launch_nv_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,

@@ -1,0 +1,355 @@
+// MS-EDEN: unbiased NVFP4 quantization for the backward pass, in two passes
+// (post hoc range alignment), on gfx950.
+//
+// Sources: "Quartet II: Accurate LLM Pre-Training in NVFP4 by Improved Unbiased
+// Gradient Estimation" -- "MS-EDEN: Microscaling EDEN" (RHT over chunks of
+// 128, RTN NVFP4 with a clip factor s, EDEN correction S per chunk, group
+// scales replaced by SR_FP8(S * scale)), "The EDEN Technique and Its Precision
+// Bottleneck" (S = <x, x> / <x, Q(x)>), and "Kernel Speedups on NVIDIA
+// Blackwell Hardware" (post hoc range alignment: pass 1 quantizes against
+// extended-range pseudo-scales and finds the global range and the
+// corrections; pass 2 reads only the scales, shifts them into FP8 range and
+// rounds them stochastically).
+//
+// What is computed (per 128-chunk of the GEMM inner dimension):
+//   y = fl(H (s o x) * c), c = fl32(1/sqrt(128)), butterflies h = 1 .. 64;
+//   p_g = 4-significant-bit RNE of fl(max|y_g| / s) (E8M3 pseudo-scale);
+//   q_i = E2M1 RNE (saturating) of fl(y_i / p_g); r_i = val(q_i) * p_g;
+//   S = fl(sum fl(z_i^2) / sum fl(z_i t_i)), z = y 2^-E, t = r 2^-E with
+//   2^E <= max|y| < 2^(E+1) over the chunk (pairwise trees in index order);
+//   v_g = fl(S * p_g); pass 2: tensor scale 2^k (least k with max v * 2^-k
+//   <= 256) and group scale SR_E4M3(v_g * 2^-k) with a counter-hash uniform.
+//
+// Design (MI355X): four lanes own one chunk, 32 elements each (element
+// 32 l + i in lane l of the quad): FWHT stages 1..16 in registers, stages 32
+// and 64 through lane shuffles within the quad; the dot products are the
+// lane's pairwise tree followed by the quad tree, which is the chunk's
+// pairwise tree.  Row axis: lanes read their 64 input bytes straight from
+// HBM.  Column axis (the transposed operand): a 128 x 64 bf16 tile staged in
+// LDS, each quad reading one column.  Pass 1 writes the codes, v (fp32, one
+// per 16) and the global max of v; pass 2 touches only the scales.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4mx_internal.h"
+
+namespace fp4mx {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;  // fl32(1/sqrt(128)), bits 0x3DB504F3
+
+__device__ __forceinline__ uint32_t hash32(uint32_t h) {  // MurmurHash3 fmix32
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  return h;
+}
+
+// E2M1 code (sign in bit 3) of RNE(v), saturating, by the hardware converter.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, 0.0f, 1.0f, 0) & 0xFu;
+}
+
+__device__ __forceinline__ float e2m1_mag(uint32_t q) {  // 0, .5, 1, 1.5, 2, 3, 4, 6
+  const uint32_t e = q >> 1, m = q & 1u;
+  return e == 0 ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
+}
+
+// fp32 rounded to 4 significant bits (nearest, ties to even) on its encoding.
+__device__ __forceinline__ float e8m3_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return __uint_as_float((b + 0x7FFFFu + ((b >> 20) & 1u)) & ~0xFFFFFu);
+}
+
+// Pairwise fp32 tree over 32 values (pairs (2i, 2i+1), then pairs of sums).
+__device__ __forceinline__ float tree32(float (&v)[32]) {
+#pragma unroll
+  for (int w = 32; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  return v[0];
+}
+
+// The quad's part of a chunk: t[32] holds elements 32 l4 + i of the chunk
+// (already sign-flipped, as fp32).  Computes the codes of the lane's 32
+// elements, v for its two 16-groups and the chunk's S (same in all 4 lanes).
+__device__ __forceinline__ void msedn_core(float (&t)[32], int l4, float clip_s,
+                                           uint32_t (&codes)[4], float (&v)[2], float& S) {
+  // FWHT stages h = 1 .. 16 within the lane
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i & h) continue;
+      const float a = t[i], b = t[i + h];
+      t[i] = a + b;
+      t[i + h] = a - b;
+    }
+  }
+  // stages h = 32 (lane l4 ^ 1) and h = 64 (lane l4 ^ 2): the lower lane keeps
+  // a + b, the upper lane a - b with a from the lower lane
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int bit = 1 << st;
+    const bool upper = (l4 & bit) != 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float o = __shfl_xor(t[i], bit, 64);
+      t[i] = upper ? o - t[i] : t[i] + o;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) t[i] = t[i] * kInvSqrt128;
+
+  float num[32], den[32];
+  float am2[2];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, __builtin_fabsf(t[16 * gi + i]));
+    am2[gi] = am;
+  }
+  // chunk exponent E: 2^E <= max|y| < 2^(E+1) (0 for a zero chunk); the dot
+  // products use y * 2^-E so no square overflows
+  float cm = fmaxf(am2[0], am2[1]);
+  cm = fmaxf(cm, __shfl_xor(cm, 1, 64));
+  cm = fmaxf(cm, __shfl_xor(cm, 2, 64));
+  const uint32_t cb = __float_as_uint(cm);
+  const int E = cb == 0 ? 0 : (cb >= 0x800000u ? (int)(cb >> 23) - 127 : (31 - __builtin_clz(cb)) - 149);
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const float p = e8m3_rne(am2[gi] / clip_s);  // IEEE division
+    v[gi] = p;
+    // q = E2M1_RNE(fl(y / p)): fl(y * fl(1/p)) is within 3 ulp of fl(y / p),
+    // so equal codes at v (1 -+ 2^-21) settle it; otherwise divide exactly
+    uint32_t q[16];
+    const float rcp = p > 0.0f ? 1.0f / p : 0.0f;
+    bool exact = !(p > 0.0f) || !(rcp < __builtin_inff());
+    if (!exact) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float w = t[16 * gi + i] * rcp;
+        const uint32_t pr = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
+            0u, w * (1.0f - 0x1p-21f), w * (1.0f + 0x1p-21f), 1.0f, 0);
+        q[i] = pr & 0xFu;
+        exact |= (pr & 0xFu) != ((pr >> 4) & 0xFu);
+      }
+    }
+    if (exact) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        q[i] = p > 0.0f ? e2m1_code(t[16 * gi + i] / p) : (__float_as_uint(t[16 * gi + i]) >> 28) & 8u;
+    }
+    codes[2 * gi] = codes[2 * gi + 1] = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      codes[2 * gi + i / 8] |= q[i] << (4 * (i % 8));
+      const float y = t[16 * gi + i];
+      const float r = __uint_as_float(__float_as_uint(e2m1_mag(q[i] & 7u)) | ((q[i] & 8u) << 28)) * p;
+      const float z = __builtin_ldexpf(y, -E), zr = __builtin_ldexpf(r, -E);
+      num[16 * gi + i] = z * z;
+      den[16 * gi + i] = z * zr;
+    }
+  }
+  float sn = tree32(num), sd = tree32(den);
+  // quad tree: (l0 + l1) + (l2 + l3); fp32 addition commutes, so every lane
+  // ends with the same value
+  sn = sn + __shfl_xor(sn, 1, 64);
+  sd = sd + __shfl_xor(sd, 1, 64);
+  sn = sn + __shfl_xor(sn, 2, 64);
+  sd = sd + __shfl_xor(sd, 2, 64);
+  S = sd > 0.0f ? sn / sd : 1.0f;  // IEEE division
+  v[0] = S * v[0];
+  v[1] = S * v[1];
+}
+
+__device__ __forceinline__ void block_max_atomic(float m, uint32_t* gmax) {
+  uint32_t b = __float_as_uint(m);  // non-negative: orders as unsigned
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) b = max(b, (uint32_t)__shfl_xor((int)b, off, 64));
+  __shared__ uint32_t wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = b;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(gmax, max(max(wm[0], wm[1]), max(wm[2], wm[3])));
+}
+
+struct Mask128 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ void unpack_signed(const uint32_t (&wd)[16], uint32_t mask, float (&t)[32]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t w = wd[j] ^ ((((mask >> (2 * j)) & 1u) << 15) | (((mask >> (2 * j + 1)) & 1u) << 31));
+    t[2 * j] = __uint_as_float(w << 16);
+    t[2 * j + 1] = __uint_as_float(w & 0xFFFF0000u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1, row axis: thread = 32 elements; quad = one 128-chunk of one row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void msedn_pass1_row(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, Mask128 mask,
+    float clip_s, uint8_t* __restrict__ codes, float* __restrict__ vbuf,
+    float* __restrict__ eden_s, uint32_t* __restrict__ gmax, FastDiv qdiv, uint32_t nthreads) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  const bool live = t < nthreads;  // every lane takes part in the shuffles
+  const uint32_t tt = live ? t : 0u;
+  const int l4 = (int)(tt & 3u);
+  const uint32_t quad = tt >> 2;                 // chunk index
+  const uint32_t row32 = fastdiv(quad, qdiv);     // qdiv.d = chunks per row
+  const int64_t row = row32, ch = quad - row32 * qdiv.d;
+  const int64_t c0 = ch * 128 + 32 * l4;          // first column of this lane
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ld + c0);
+  uint32_t wd[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 v = __builtin_nontemporal_load(src + q);
+    wd[4 * q] = v.x; wd[4 * q + 1] = v.y; wd[4 * q + 2] = v.z; wd[4 * q + 3] = v.w;
+  }
+  float tv[32];
+  unpack_signed(wd, mask.w[l4], tv);
+  uint32_t cw[4];
+  float v[2], S;
+  msedn_core(tv, l4, clip_s, cw, v, S);
+  if (live) {
+    *reinterpret_cast<u32x4*>(codes + row * (cols / 2) + c0 / 2) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+    *reinterpret_cast<float2*>(vbuf + row * (cols / 16) + c0 / 16) = make_float2(v[0], v[1]);
+    if (eden_s && l4 == 0) eden_s[row * (cols / 128) + ch] = S;
+  }
+  block_max_atomic(live ? fmaxf(v[0], v[1]) : 0.0f, gmax);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1, column axis: 128 x 64 bf16 tile in LDS; quad = one column's chunk.
+// Output operand row = input column, output column = input row.
+// ---------------------------------------------------------------------------
+constexpr int kCPitch = 132;  // bytes per LDS row: 2-way conflicts between quads at most
+
+__global__ __launch_bounds__(256) void msedn_pass1_col(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, Mask128 mask,
+    float clip_s, uint8_t* __restrict__ codes, float* __restrict__ vbuf,
+    float* __restrict__ eden_s, uint32_t* __restrict__ gmax) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kCPitch];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 128, cb = (int64_t)blockIdx.y * 64;
+  const int nc = (int)min<int64_t>(64, cols - cb);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int id = tid + 256 * it;  // 1024 chunks of 8 bf16
+    const int r = id >> 3, chk = id & 7;
+    if (chk * 8 < nc) {
+      const u32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(x + (r0 + r) * ld + cb + chk * 8));
+      uint32_t* d = reinterpret_cast<uint32_t*>(tile + r * kCPitch + chk * 16);
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+  }
+  __syncthreads();
+  const int c = tid >> 2, l4 = tid & 3;
+  const bool live = c < nc;
+  const int cc = live ? c : 0;
+  float tv[32];
+  const uint32_t m = mask.w[l4];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t h = *reinterpret_cast<const uint16_t*>(tile + (32 * l4 + i) * kCPitch + 2 * cc);
+    tv[i] = __uint_as_float((h << 16) ^ (((m >> i) & 1u) << 31));
+  }
+  uint32_t cw[4];
+  float v[2], S;
+  msedn_core(tv, l4, clip_s, cw, v, S);
+  if (live) {
+    const int64_t orow = cb + c, ocol = r0 + 32 * l4;
+    *reinterpret_cast<u32x4*>(codes + orow * (rows / 2) + ocol / 2) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+    *reinterpret_cast<float2*>(vbuf + orow * (rows / 16) + ocol / 16) = make_float2(v[0], v[1]);
+    if (eden_s && l4 == 0) eden_s[orow * (rows / 128) + r0 / 128] = S;
+  }
+  block_max_atomic(live ? fmaxf(v[0], v[1]) : 0.0f, gmax);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: thread = one group scale.  k = least integer with max * 2^-k <= 256;
+// scale = SR_E4M3(v * 2^-k) with u = (r >> 8) * 2^-24, r = hash of the
+// scale's flat index in the output operand.
+// ---------------------------------------------------------------------------
+__global__ void msedn_zero(uint32_t* p) { *p = 0u; }
+
+__global__ __launch_bounds__(256) void msedn_pass2(const float* __restrict__ vbuf,
+                                                   const uint32_t* __restrict__ gmax,
+                                                   uint64_t nscales, uint32_t key_lo,
+                                                   uint32_t key_hi, uint8_t* __restrict__ scales,
+                                                   float* __restrict__ tensor_scale) {
+  const uint32_t mb = *gmax;
+  int k = 0;
+  if (mb != 0) {
+    // ceil(log2 max): normal 1.f * 2^(e-127); subnormal mb * 2^-149
+    const int e = (int)(mb >> 23);
+    const int lg = e != 0 ? e - 127 + ((mb & 0x7FFFFFu) != 0 ? 1 : 0)
+                          : (mb == 1u ? 0 : 32 - __builtin_clz(mb - 1u)) - 149;
+    k = lg - 8;
+  }
+  const uint64_t t = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  if (t == 0) *tensor_scale = __builtin_ldexpf(1.0f, k);
+  if (t >= nscales) return;
+  const float w = __builtin_ldexpf(vbuf[t], -k);
+  const uint32_t kmix = key_lo ^ hash32((uint32_t)(t >> 32) ^ key_hi);
+  const uint32_t r = hash32((uint32_t)t ^ kmix);
+  const uint32_t b = __float_as_uint(w);
+  uint32_t code;
+  if (w >= 0x1p-6f) {
+    // normal E4M3: floor code from exponent and top 3 fraction bits, up iff
+    // (r >> 12) < the 20 fraction bits below them
+    const uint32_t fl = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+    code = fl + (((r >> 12) < (b & 0xFFFFFu)) ? 1u : 0u);
+    code = min(code, 0x7Eu);  // saturate at 448
+  } else {
+    // subnormal step 2^-9: t = w * 2^9 < 8, up iff (r >> 8) < frac(t) * 2^24
+    const float tt = w * 512.0f;
+    const float a = __builtin_floorf(tt);
+    code = (uint32_t)a + (((float)(r >> 8) < (tt - a) * 0x1p24f) ? 1u : 0u);
+  }
+  scales[t] = (uint8_t)code;
+}
+
+}  // namespace
+
+void msedn_sign_words(uint64_t seed, uint32_t gemm_id, uint32_t (&w)[4]) {
+  const uint64_t a = splitmix64(seed ^ ((uint64_t)(0x5200u + 2u * gemm_id) << 32));
+  const uint64_t b = splitmix64(seed ^ ((uint64_t)(0x5201u + 2u * gemm_id) << 32));
+  w[0] = (uint32_t)a; w[1] = (uint32_t)(a >> 32); w[2] = (uint32_t)b; w[3] = (uint32_t)(b >> 32);
+}
+
+hipError_t launch_msedn(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                        float clip_s, uint64_t seed, uint32_t gemm_id, uint32_t stream,
+                        uint8_t* codes, uint8_t* scales, float* tensor_scale, float* eden_s,
+                        float* vbuf, uint32_t* gmax, hipStream_t s) {
+  Mask128 m;
+  msedn_sign_words(seed, gemm_id, m.w);
+  const RngKey key = make_key(seed, stream);
+  hipLaunchKernelGGL(msedn_zero, dim3(1), dim3(1), 0, s, gmax);  // a kernel: safe under capture
+  int64_t nscales;
+  if (axis == FP4MX_AXIS_ROW) {
+    const int64_t cpr = cols / 128;
+    const uint64_t threads = (uint64_t)rows * (uint64_t)cpr * 4u;
+    if (threads >= (1ull << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(msedn_pass1_row, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       x, rows, cols, ld, m, clip_s, codes, vbuf, eden_s, gmax,
+                       make_fastdiv((uint32_t)cpr), (uint32_t)threads);
+    nscales = rows * (cols / 16);
+  } else {
+    hipLaunchKernelGGL(msedn_pass1_col, dim3((unsigned)(rows / 128), (unsigned)((cols + 63) / 64)),
+                       dim3(256), 0, s, x, rows, cols, ld, m, clip_s, codes, vbuf, eden_s, gmax);
+    nscales = cols * (rows / 16);
+  }
+  hipLaunchKernelGGL(msedn_pass2, dim3((unsigned)((nscales + 255) / 256)), dim3(256), 0, s, vbuf,
+                     gmax, (uint64_t)nscales, key.lo, key.hi, scales, tensor_scale);
+  return hipGetLastError();
+}
+
+}  // namespace fp4mx

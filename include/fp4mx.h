@@ -231,6 +231,52 @@ FP4MX_API size_t fp4nv_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
 FP4MX_API int fp4nv_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t k,
                      float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Unbiased NVFP4 quantization for the backward pass: MS-EDEN.
+ * Source: "Quartet II: Accurate LLM Pre-Training in NVFP4 by Improved
+ * Unbiased Gradient Estimation" -- "MS-EDEN: Microscaling EDEN" (RHT over
+ * chunks of 128, RTN NVFP4 with clip factor s, EDEN correction S per chunk,
+ * group scales SR_FP8(S * scale)), "The EDEN Technique and Its Precision
+ * Bottleneck" (S = <x, x> / <x, Q(x)>), "Kernel Speedups on NVIDIA Blackwell
+ * Hardware" (post hoc range alignment in two passes).
+ * Per 128-chunk along the operand's inner dimension (rows of x for AXIS_ROW,
+ * columns of x for AXIS_COL, whose output is the transposed operand):
+ *   y = fl(H (s o x) c), c = fl32(1/sqrt(128)), 128-bit sign pattern of
+ *   (seed, gemm_id); p = E8M3_RNE(fl(max|y_16| / clip_s)) (4 significant bits);
+ *   q = E2M1_RNE_sat(fl(y / p)); S = fl(sum y^2 / sum y * q p) (pairwise fp32);
+ *   v = fl(S p); tensor scale g = 2^k, k least with max v 2^-k <= 256;
+ *   group scale = SR_E4M3(v 2^-k) with u = (r >> 8) 2^-24 from the counter hash
+ *   of (seed, rng_stream) at the scale's flat index in the output operand.
+ * Output operand layout as fp4nv_quantize46 (codes [R][C/2], E4M3 [R][C/16],
+ * one fp32 g in device memory).  E[q * scale * g] = S * q * p.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes for fp4nv_msedn_quantize (fp32 v per 16-group + max). */
+FP4MX_API size_t fp4nv_msedn_workspace_bytes(int64_t rows, int64_t cols);
+
+/* MS-EDEN of x bf16 [rows][ld].  axis ROW: cols % 128 == 0, output [rows][cols];
+ * axis COL: rows % 128 == 0, output [cols][rows].  clip_s > 0 (6 = no clip
+ * beyond E8M3 rounding).  eden_s: optional fp32 [out_rows][out_cols/128]
+ * receiving S (NULL to skip).  Errors as fp4mx_quantize. */
+FP4MX_API int fp4nv_msedn_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                         float clip_s, uint64_t seed, uint32_t gemm_id, uint32_t rng_stream,
+                         uint8_t* codes, uint8_t* scales, float* tensor_scale, float* eden_s,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for fp4nv_linear_bwd. */
+FP4MX_API size_t fp4nv_linear_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* NVFP4 backward of Y = X W^T with MS-EDEN operands (clip 6), per "The
+ * Complete Quartet II Computation Graph" (RHT on the inner dimension of each
+ * GEMM, no inverse, no rescale):
+ *   dX [m][k] = gemm(MSEDEN_row(dY; gemm 1, stream 5), MSEDEN_col(W; gemm 1, stream 6))
+ *   dW [n][k] = gemm(MSEDEN_col(dY; gemm 2, stream 7), MSEDEN_col(X; gemm 2, stream 8))
+ * dy bf16 [m][n], x bf16 [m][k], w bf16 [n][k]; m % 128 == 0, n % 128 == 0,
+ * k % 32 == 0.  The GEMMs are fp4nv_gemm (FP8 staging). */
+FP4MX_API int fp4nv_linear_bwd(const void* dy, const void* x, const void* w, int64_t m, int64_t n,
+                     int64_t k, uint64_t seed, float* dx, float* dw, void* ws, size_t ws_bytes,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,151 @@
+"""GPU parity of MS-EDEN (unbiased NVFP4 backward quantization) and of the
+NVFP4 linear backward built on it, against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_microscaled_quantized_amd as fq
+from fp4_microscaled_quantized_amd import synth
+from oracle import msedn, nvfp4
+
+from gpu_util import assert_bytes_equal, cpu, dev_bf16, host_f32, log, rel_fro
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _check_quant(bits, axis, seed, gemm_id, stream, clip=6.0):
+    x = host_f32(bits)
+    src = x if axis == fq.ROW else np.ascontiguousarray(x.T)
+    words = msedn.sign_mask128(seed, gemm_id)
+    codes, sc, g, S = msedn.msedn_quantize(src, words, seed=seed, stream=stream, s=clip)
+    out, s_gpu = fq.nv_msedn_quantize(dev_bf16(bits), axis=axis, seed=seed, gemm_id=gemm_id,
+                                      stream=stream, clip=clip, want_s=True)
+    torch.cuda.synchronize()
+    assert cpu(out.tensor_scale)[0] == g, (cpu(out.tensor_scale)[0], g)
+    assert_bytes_equal(cpu(s_gpu).view(np.uint32), S.view(np.uint32), "EDEN S")
+    assert_bytes_equal(cpu(out.codes), codes, "ms-eden codes")
+    assert_bytes_equal(cpu(out.scales), sc, "ms-eden scales")
+
+
+@pytest.mark.parametrize("shape", [(32, 128), (64, 256), (96, 384), (160, 1024)])
+@pytest.mark.parametrize("seed", [0, 5])
+def test_msedn_row_bit_exact(shape, seed):
+    log("ms-eden row", shape, seed)
+    _check_quant(synth.normal_with_outliers(shape, seed, 2), fq.ROW, seed, 1, 5)
+
+
+@pytest.mark.parametrize("shape", [(128, 64), (256, 96), (384, 160), (128, 32), (256, 224)])
+def test_msedn_col_bit_exact(shape):
+    log("ms-eden col", shape)
+    _check_quant(synth.normal_with_outliers(shape, 3, 0), fq.COL, 3, 2, 8)
+
+
+def test_msedn_edge_cases():
+    rs = np.random.default_rng(12)
+    x = (rs.standard_normal((64, 256)) * np.exp(rs.uniform(-20, 20, (64, 1)))).astype(np.float32)
+    x[1] = 0.0                      # zero row
+    x[2, :128] = 0.0                # zero chunk
+    x[3, 5] = 1e30                  # one huge value
+    x[4] = 1e-30                    # tiny row (fp32-subnormal products)
+    bits = synth.f32_to_bf16_bits(x)
+    _check_quant(bits, fq.ROW, 9, 1, 5)
+    _check_quant(np.ascontiguousarray(np.vstack([bits, bits])[:, :96]), fq.COL, 9, 2, 7)
+    # clip factor below 6 (clipping in the pseudo-scale domain)
+    _check_quant(synth.normal((64, 256), 1.0, 13, 0), fq.ROW, 13, 1, 5, clip=4.0)
+
+
+def test_msedn_table1_on_gpu(golden):
+    """MSE of the GPU's MS-EDEN on N(0,1) matches the page's 9.8e-3."""
+    want = {r[0]: float(r[1]) for r in golden("nvfp4_table1_mse.txt")}
+    x = np.random.default_rng(0).standard_normal((1024, 1024)).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(x)
+    out = fq.nv_msedn_quantize(dev_bf16(bits), axis=fq.ROW, seed=0, gemm_id=1, stream=5)
+    y = msedn.rht128(host_f32(bits), msedn.sign_mask128(0, 1))
+    d = nvfp4.dequantize(cpu(out.codes), cpu(out.scales), cpu(out.tensor_scale)[0])
+    mse = np.mean((d - y) ** 2) * 1e3
+    log("  ms-eden mse x1e3", mse)
+    assert abs(mse - want["ms_eden"]) < 0.3
+
+
+def _oracle_bwd(dyf, xf, wf, seed):
+    w1, w2 = msedn.sign_mask128(seed, 1), msedn.sign_mask128(seed, 2)
+    a = msedn.msedn_quantize(dyf, w1, seed=seed, stream=5)[:3]
+    b = msedn.msedn_quantize(np.ascontiguousarray(wf.T), w1, seed=seed, stream=6)[:3]
+    dx = nvfp4.gemm_fp8_staged(*a, *b)
+    c = msedn.msedn_quantize(np.ascontiguousarray(dyf.T), w2, seed=seed, stream=7)[:3]
+    d = msedn.msedn_quantize(np.ascontiguousarray(xf.T), w2, seed=seed, stream=8)[:3]
+    dw = nvfp4.gemm_fp8_staged(*c, *d)
+    return dx, dw
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 128, 64), (256, 384, 160), (128, 256, 512)])
+def test_nv_linear_bwd_small(m, n, k):
+    log("nv bwd", m, n, k)
+    xb = synth.normal((m, k), 1.0, 4, 0)
+    wb = synth.normal((n, k), 0.02, 4, 1)
+    dyb = synth.normal((m, n), 1e-3, 4, 2)
+    dx, dw = fq.nv_linear_bwd(dev_bf16(dyb), dev_bf16(xb), dev_bf16(wb), seed=11)
+    torch.cuda.synchronize()
+    rdx, rdw = _oracle_bwd(host_f32(dyb), host_f32(xb), host_f32(wb), 11)
+    edx, edw = rel_fro(cpu(dx), rdx), rel_fro(cpu(dw), rdw)
+    log("  rel err dx %.2e dw %.2e" % (edx, edw))
+    assert edx <= TOL and edw <= TOL
+
+
+def test_nv_linear_bwd_unbiased_on_gpu():
+    """Mean of B GPU backward estimates (different seeds) -> exact gradients."""
+    m, n, k = 128, 128, 64
+    xb = synth.normal((m, k), 1.0, 5, 0)
+    wb = synth.normal((n, k), 1.0, 5, 1)
+    dyb = synth.normal((m, n), 1.0, 5, 2)
+    x, w, dy = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb)
+    ex_dx = host_f32(dyb).astype(np.float64) @ host_f32(wb).astype(np.float64)
+    ex_dw = host_f32(dyb).T.astype(np.float64) @ host_f32(xb).astype(np.float64)
+    dxs, dws = [], []
+    for seed in range(256):
+        dx, dw = fq.nv_linear_bwd(dy, x, w, seed=seed)
+        dxs.append(cpu(dx))
+        dws.append(cpu(dw))
+    for ests, ex in ((np.array(dxs), ex_dx), (np.array(dws), ex_dw)):
+        def mse(B):
+            mm = ests[: (len(ests) // B) * B].reshape(-1, B, *ex.shape).mean(axis=1)
+            return np.mean((mm - ex) ** 2)
+        e1, e16, e64 = mse(1), mse(16), mse(64)
+        log("  1/B mse", e1, e16, e64)
+        assert e16 < e1 / 8 and e64 < e1 / 25
+
+
+@pytest.mark.timeout(600)
+def test_nv_linear_bwd_full_size_sampled():
+    """M=8192, N=K=4096 (the Quartet layer's dY, X, W): sampled dX / dW entries
+    against oracle operands quantized row by row with the full tensors' ranges."""
+    d = synth.quartet_linear(0)
+    xb, wb, dyb = d["x"], d["w"], d["dy"]
+    m, k = xb.shape
+    n = wb.shape[0]
+    seed = 0
+    log("nv bwd full-size", m, n, k)
+    dx, dw = fq.nv_linear_bwd(dev_bf16(dyb), dev_bf16(xb), dev_bf16(wb), seed=seed)
+    torch.cuda.synchronize()
+    dx, dw = cpu(dx), cpu(dw)
+    xf, wf, dyf = host_f32(xb), host_f32(wb), host_f32(dyb)
+    w1, w2 = msedn.sign_mask128(seed, 1), msedn.sign_mask128(seed, 2)
+    rs = np.random.default_rng(321)
+    ri = np.sort(rs.choice(m, 24, replace=False))
+    cj = np.sort(rs.choice(n, 24, replace=False))
+    ck = np.sort(rs.choice(k, 24, replace=False))
+    wt, dyt, xt = np.ascontiguousarray(wf.T), np.ascontiguousarray(dyf.T), np.ascontiguousarray(xf.T)
+    # global range exponents of the four operands (whole tensors), then rows
+    k_a = msedn.msedn_range_exponent(dyf, w1)
+    k_b = msedn.msedn_range_exponent(wt, w1)
+    a = msedn.msedn_quantize(dyf[ri], w1, seed=seed, stream=5, row_ids=ri, k=k_a)[:3]
+    b = msedn.msedn_quantize(wt[ck], w1, seed=seed, stream=6, row_ids=ck, k=k_b)[:3]
+    edx = rel_fro(dx[np.ix_(ri, ck)], nvfp4.gemm_fp8_staged(*a, *b))
+    k_c = msedn.msedn_range_exponent(dyt, w2)
+    k_d = msedn.msedn_range_exponent(xt, w2)
+    c = msedn.msedn_quantize(dyt[cj], w2, seed=seed, stream=7, row_ids=cj, k=k_c)[:3]
+    dd = msedn.msedn_quantize(xt[ck], w2, seed=seed, stream=8, row_ids=ck, k=k_d)[:3]
+    edw = rel_fro(dw[np.ix_(cj, ck)], nvfp4.gemm_fp8_staged(*c, *dd))
+    log("  sampled rel err dx %.2e dw %.2e" % (edx, edw))
+    assert edx <= TOL and edw <= TOL
