@@ -281,6 +281,64 @@ def time_nvfp4(steps, warmup):
             "TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
 
 
+def _time_calls(call, steps, warmup):
+    import torch
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(steps):
+        call(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / steps
+
+
+def time_nvfp4_bwd(steps, warmup):
+    """NVFP4 backward with MS-EDEN operands on the Quartet layer (dX and dW,
+    4 MS-EDEN quantizations + 2 FP8-staged GEMMs), and the unbiased quantizers
+    alone on dY (8192 x 4096) against their algorithmic bytes."""
+    import torch
+    import fp4_microscaled_quantized_amd as fq
+    from fp4_microscaled_quantized_amd import synth
+    from fp4_microscaled_quantized_amd.binding import _ptr, _stream
+    d = synth.quartet_linear(0)
+    x, w, dy = dev_bf16(d["x"]), dev_bf16(d["w"]), dev_bf16(d["dy"])
+    m, k = x.shape
+    n = w.shape[0]
+    L = fq.lib()
+    ws = torch.empty(L.fp4nv_linear_bwd_workspace_bytes(m, n, k), dtype=torch.uint8, device="cuda")
+    dx = torch.empty((m, k), dtype=torch.float32, device="cuda")
+    dw = torch.empty((n, k), dtype=torch.float32, device="cuda")
+    ms = _time_calls(lambda i: fq.nv_linear_bwd(dy, x, w, seed=i, ws=ws, dx=dx, dw=dw), steps, warmup)
+    res = {"workload": "NVFP4 MS-EDEN linear bwd dX,dW M=8192 N=K=4096", "ms": round(ms, 4),
+           "TFLOP/s": round(4.0 * m * n * k / (ms * 1e-3) / 1e12, 1)}
+    del ws
+    R, C = dy.shape
+    codes = torch.empty((R, C // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((R, C // 16), dtype=torch.uint8, device="cuda")
+    g = torch.empty(1, dtype=torch.float32, device="cuda")
+    qws = torch.empty(max(L.fp4nv_msedn_workspace_bytes(R, C), L.fp4nv_quantize_workspace_bytes(R, C)),
+                      dtype=torch.uint8, device="cuda")
+    st = _stream(dy.device)
+    alg = R * C * (2 + 0.5 + 1 / 16)  # bf16 in, E2M1 codes + E4M3 scales out
+    qs = {}
+    for name, call in (
+        ("ms_eden_row", lambda i: L.fp4nv_msedn_quantize(_ptr(dy), R, C, C, fq.ROW, 6.0, i, 1, 5, _ptr(codes),
+                                                         _ptr(scales), _ptr(g), None, _ptr(qws),
+                                                         qws.numel(), st)),
+        ("sr_baseline_row", lambda i: L.fp4nv_sr_quantize(_ptr(dy), R, C, C, i, 5, _ptr(codes), _ptr(scales),
+                                                          _ptr(g), _ptr(qws), qws.numel(), st))):
+        assert call(0) == 0
+        qms = _time_calls(call, max(steps, 20), warmup)
+        qs[name] = {"us": round(qms * 1e3, 2), "GB/s": round(alg / (qms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(alg / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    res["quantizers_8192x4096"] = qs
+    res["quantizer_algorithmic_bytes"] = int(alg)
+    return res
+
+
 def cpu_baseline(rows=256):
     """The oracle's linear fwd+bwd on the first `rows` tokens of the headline workload."""
     from fp4_microscaled_quantized_amd import synth
@@ -361,6 +419,8 @@ def main():
         out["quantizer"] = time_quantizer(max(a.steps, 20), a.warmup)
         torch.cuda.empty_cache()
         out["nvfp4"] = time_nvfp4(max(a.steps // 2, 5), 2)
+        torch.cuda.empty_cache()
+        out["nvfp4_bwd_ms_eden"] = time_nvfp4_bwd(max(a.steps // 2, 5), 2)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))

@@ -52,6 +52,7 @@ _SIGS = {
     "fp4nv_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4nv_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4nv_linear_fwd": (_INT, [_P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "fp4nv_sr_quantize": (_INT, [_P, _I64, _I64, _I64, _U64, _U32, _P, _P, _P, _P, _SZ, _P]),
     "fp4nv_msedn_workspace_bytes": (_SZ, [_I64, _I64]),
     "fp4nv_msedn_quantize": (_INT, [_P, _I64, _I64, _I64, _INT, C.c_float, _U64, _U32, _U32, _P, _P,
                                     _P, _P, _P, _SZ, _P]),
@@ -257,6 +258,20 @@ def nv_linear_fwd(x, w, ws=None, out=None):
     _check(lib().fp4nv_linear_fwd(_ptr(x), _ptr(w), m, n, k, _ptr(y), _ptr(ws), ws.numel(),
                                   _stream(dev)))
     return y
+
+
+def nv_sr_quantize(x, seed=0, stream=1) -> NVTensor:
+    """Standard NVFP4 stochastic rounding (16/17 guard) of x along rows."""
+    R, Cc, ld = _bf16_2d(x)
+    dev = x.device
+    out = NVTensor(torch.empty((R, Cc // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((R, Cc // 16), dtype=torch.uint8, device=dev),
+                   torch.empty(1, dtype=torch.float32, device=dev))
+    ws = torch.empty(lib().fp4nv_quantize_workspace_bytes(R, Cc), dtype=torch.uint8, device=dev)
+    _check(lib().fp4nv_sr_quantize(_ptr(x), R, Cc, ld, int(seed), stream, _ptr(out.codes),
+                                   _ptr(out.scales), _ptr(out.tensor_scale), _ptr(ws), ws.numel(),
+                                   _stream(dev)))
+    return out
 
 
 def nv_msedn_quantize(x, axis=ROW, seed=0, gemm_id=1, stream=5, clip=6.0, want_s=False):

@@ -342,6 +342,28 @@ int fp4nv_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t
   return nv_gemm_impl(xq, xs, gx, wq, wsc, gw, m, n, k, y, n, cv.p, s);
 }
 
+int fp4nv_sr_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
+                      uint32_t rng_stream, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !codes || !scales || !tensor_scale) return FP4MX_E_NULL;
+  if (!dim_ok(rows) || !dim_ok(cols) || ld < cols) return FP4MX_E_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scales & 1u) || ld % 8 != 0 ||
+      ((uintptr_t)tensor_scale & 3u))
+    return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4nv_quantize_workspace_bytes(rows, cols)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  const RngKey key = make_key(seed, rng_stream);
+  hipError_t e = launch_nv_amax(static_cast<const uint16_t*>(x), rows, cols, ld, amax, s);
+  if (e == hipSuccess)
+    e = launch_nv_sr(static_cast<const uint16_t*>(x), rows, cols, ld, amax, key.lo, key.hi, codes,
+                     scales, tensor_scale, s);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
 size_t fp4nv_msedn_workspace_bytes(int64_t rows, int64_t cols) {
   if (!dim_ok(rows) || !dim_ok(cols)) return 0;
   return round_up((size_t)rows * cols / 16 * sizeof(float)) + 256;

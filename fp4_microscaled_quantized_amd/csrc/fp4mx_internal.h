@@ -74,6 +74,10 @@ hipError_t launch_msedn(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
                         float* vbuf, uint32_t* gmax, hipStream_t s);
 void msedn_sign_words(uint64_t seed, uint32_t gemm_id, uint32_t (&w)[4]);
 
+hipError_t launch_nv_sr(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                        const uint32_t* amax_bits, uint32_t key_lo, uint32_t key_hi,
+                        uint8_t* codes, uint8_t* scales, float* tensor_scale, hipStream_t s);
+
 hipError_t launch_nv_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                           uint32_t* amax_bits, hipStream_t s);
 hipError_t launch_nv_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,

@@ -231,6 +231,17 @@ FP4MX_API size_t fp4nv_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
 FP4MX_API int fp4nv_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t k,
                      float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* Standard NVFP4 stochastic rounding (the unbiased baseline of "Quartet II
+ * ..." -- "NVFP4 Format and Standard Stochastic Rounding", 16/17 guard):
+ *   c = fl32(96/17) (6 * 16/17 rounded once); g = fl(max|x| / fl(c * 448)) (written to tensor_scale);
+ *   s16 = E4M3_RNE(fl(max|x_16| / fl(g * c))); v = fl(x / fl(s16 * g)), |v| <= 6;
+ *   q = SR onto E2M1 with u = (r >> 8) 2^-24, r the counter hash of (seed,
+ *   rng_stream) at index row * cols + col (b taken iff u < (|v| - a)/(b - a)).
+ * Layout and workspace as fp4nv_quantize46 (rows along which groups run). */
+FP4MX_API int fp4nv_sr_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                      uint64_t seed, uint32_t rng_stream, uint8_t* codes, uint8_t* scales,
+                      float* tensor_scale, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Unbiased NVFP4 quantization for the backward pass: MS-EDEN.
  * Source: "Quartet II: Accurate LLM Pre-Training in NVFP4 by Improved

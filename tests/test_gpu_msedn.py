@@ -149,3 +149,60 @@ def test_nv_linear_bwd_full_size_sampled():
     edw = rel_fro(dw[np.ix_(cj, ck)], nvfp4.gemm_fp8_staged(*c, *dd))
     log("  sampled rel err dx %.2e dw %.2e" % (edx, edw))
     assert edx <= TOL and edw <= TOL
+
+
+def _check_sr(bits, seed, stream):
+    codes, sc, g = msedn.sr_quantize(host_f32(bits), seed=seed, stream=stream)
+    out = fq.nv_sr_quantize(dev_bf16(bits), seed=seed, stream=stream)
+    torch.cuda.synchronize()
+    assert cpu(out.tensor_scale)[0] == g, (cpu(out.tensor_scale)[0], g)
+    assert_bytes_equal(cpu(out.scales), sc, "sr scales")
+    assert_bytes_equal(cpu(out.codes), codes, "sr codes")
+
+
+@pytest.mark.parametrize("shape", [(32, 32), (64, 256), (96, 1056), (352, 160)])
+@pytest.mark.parametrize("seed", [0, 21])
+def test_nv_sr_bit_exact(shape, seed):
+    log("nvfp4 sr", shape, seed)
+    _check_sr(synth.normal_with_outliers(shape, seed, 1), seed, 3)
+
+
+def test_nv_sr_edge_cases():
+    rs = np.random.default_rng(4)
+    x = (rs.standard_normal((32, 64)) * np.exp(rs.uniform(-30, 30, (32, 1)))).astype(np.float32)
+    x[1] = 0.0
+    x[2, :16] = -0.0
+    x[3, 7] = 3e38
+    x[5] = 1e-38
+    _check_sr(synth.f32_to_bf16_bits(x), 2, 1)
+    _check_sr(synth.f32_to_bf16_bits(np.zeros((32, 32), np.float32)), 2, 1)
+
+
+def test_nv_sr_table1_on_gpu(golden):
+    """MSE of the GPU's standard NVFP4 SR on N(0,1) matches the page's 23.5e-3."""
+    want = {r[0]: float(r[1]) for r in golden("nvfp4_table1_mse.txt")}
+    x = np.random.default_rng(0).standard_normal((1024, 1024)).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(x)
+    out = fq.nv_sr_quantize(dev_bf16(bits), seed=0, stream=5)
+    d = nvfp4.dequantize(cpu(out.codes), cpu(out.scales), cpu(out.tensor_scale)[0])
+    mse = np.mean((d - host_f32(bits)) ** 2) * 1e3
+    log("  sr mse x1e3", mse)
+    assert abs(mse - want["sr"]) < 0.3
+
+
+@pytest.mark.timeout(300)
+def test_nv_sr_full_size_sampled():
+    """dY of the Quartet layer (8192 x 4096): the first 1024 rows against the
+    oracle run on those rows plus one appended row that carries the whole
+    tensor's max (so g, and every RNG index row * cols + col, are the same)."""
+    dyb = synth.quartet_linear(0)["dy"]
+    out = fq.nv_sr_quantize(dev_bf16(dyb), seed=7, stream=2)
+    torch.cuda.synchronize()
+    dyf = host_f32(dyb)
+    amax = np.max(np.abs(dyf))
+    sub = np.vstack([dyf[:1024], np.full((1, dyf.shape[1]), amax, np.float32)])
+    codes, sc, g = msedn.sr_quantize(sub, seed=7, stream=2)
+    log("nvfp4 sr full-size", dyf.shape)
+    assert cpu(out.tensor_scale)[0] == g
+    assert_bytes_equal(cpu(out.codes)[:1024], codes[:1024], "sr codes, first 1024 rows")
+    assert_bytes_equal(cpu(out.scales)[:1024], sc[:1024], "sr scales, first 1024 rows")
