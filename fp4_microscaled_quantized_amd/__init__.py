@@ -4,7 +4,7 @@ layer for AMD MI355X (gfx950).
 The computation lives in ``libfp4mx.so`` (HIP kernels behind a C ABI declared
 in ``include/fp4mx.h``); ``binding`` is its thin ctypes wrapper.
 """
-from .binding import (COL, ROW, RTN, SR, FP4LinearFunction, LinearCtx, MXTensor, NVTensor,  # noqa: F401
+from .binding import (COL, QUEST_CLIP, ROW, RTN, SR, FP4LinearFunction, LinearCtx, MXTensor, NVTensor,  # noqa: F401
                       gemm, hadamard_quantize, hadamard_quantize_dual, lib, linear_bwd, linear_fwd,
                       nv_gemm, nv_linear_bwd, nv_linear_fwd, nv_msedn_quantize, nv_quantize46, nv_sr_quantize, quantize,
                       sign_mask)

@@ -17,6 +17,9 @@ LIB_PATH = os.path.join(_HERE, "libfp4mx.so")
 
 RTN, SR = 0, 1
 ROW, COL = 0, 1
+# QuEST clip factor: the minimiser over [1, 5] of E[(x - Q_c(clamp(x, -c, c)))^2]
+# for x ~ N(0,1), Q_c = E2M1 round-to-nearest on the grid scaled by c/6.
+QUEST_CLIP = 2.922475
 
 _lib = None
 

@@ -23,9 +23,14 @@ orthogonality), the RNG (published test vectors), SR (exact probabilities,
 unbiasedness), GEMM (brute-force triple loop), linear backward (expectation
 equals the exact gradient), NVFP4 RTN and RTN+4/6 (the pages' Table 1 MSEs),
 MS-EDEN and the NVFP4 SR baseline (Table 1 MSEs, the EDEN correction range,
-RHT_128 structure, unbiasedness of the scale rounding and of the product).
+RHT_128 structure, unbiasedness of the scale rounding and of the product),
+QuEST (the Gaussian objective against quadrature and Monte Carlo, its
+minimum, sigma and thresholds against fp64, reduction of clipping groups to MX
+RTN, the page's MSE ranking QuEST < RTN < SR, power-of-two invariance) and the
+Quartet backward in the rotated basis (inverse RHT against the matrix
+inverse, mask correction, re-quantization and the whole backward unbiased).
 Parity unpinned: the FP8 staging of the NVFP4 GEMM (a design of this library
 that the pages do not describe; only its self-consistency is checked).
 """
 
-from . import formats, rng, rht, mx, nvfp4, msedn  # noqa: F401
+from . import formats, rng, rht, mx, nvfp4, msedn, quest  # noqa: F401
