@@ -36,6 +36,11 @@ class CtxStruct(C.Structure):
                 ("seed", _U64)]
 
 
+class QuestCtxStruct(C.Structure):
+    _fields_ = [("xq_codes", _P), ("xq_scales", _P), ("wq_codes", _P), ("wq_scales", _P),
+                ("x_mask", _P), ("w_mask", _P), ("seed", _U64)]
+
+
 _SIGS = {
     "fp4mx_status_string": (C.c_char_p, [_INT]),
     "fp4mx_last_hip_error": (_INT, []),
@@ -49,6 +54,15 @@ _SIGS = {
     "fp4mx_ctx_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4mx_linear_fwd": (_INT, [_P, _P, _I64, _I64, _I64, _U64, _P, C.POINTER(CtxStruct), _P, _SZ, _P]),
     "fp4mx_linear_bwd": (_INT, [_P, C.POINTER(CtxStruct), _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "fp4mx_quest_quantize": (_INT, [_P, _I64, _I64, _I64, C.c_float, _U32, _P, _P, _P, _P]),
+    "fp4mx_requantize": (_INT, [_P, _P, _I64, _I64, _INT, _U32, _U64, _U32, _P, _P, _P]),
+    "fp4mx_unmask_inverse_hadamard": (_INT, [_P, _I64, _I64, _I64, _P, _U32, _P]),
+    "fp4mx_quest_ctx_bytes": (_SZ, [_I64, _I64, _I64]),
+    "fp4mx_quest_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "fp4mx_quest_linear_fwd": (_INT, [_P, _P, _I64, _I64, _I64, C.c_float, _U64, _P,
+                                      C.POINTER(QuestCtxStruct), _P]),
+    "fp4mx_quest_linear_bwd": (_INT, [_P, C.POINTER(QuestCtxStruct), _I64, _I64, _I64, _P, _P, _P, _SZ,
+                                      _P]),
     "fp4nv_quantize_workspace_bytes": (_SZ, [_I64, _I64]),
     "fp4nv_quantize46": (_INT, [_P, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _SZ, _P]),
     "fp4nv_gemm": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _SZ, _P]),
@@ -214,6 +228,87 @@ def linear_bwd(dy, ctx: LinearCtx, ws=None, dx=None, dw=None):
     st = ctx.as_struct()
     _check(lib().fp4mx_linear_bwd(_ptr(dy), C.byref(st), m, n, k, _ptr(dx), _ptr(dw), _ptr(ws),
                                   ws.numel(), _stream(dev)))
+    return dx, dw
+
+
+# ------------------------------ QuEST --------------------------------------
+
+def quest_quantize(x, clip=QUEST_CLIP, mask=0):
+    """QuEST MXFP4 quantization along rows after the RHT: (MXTensor, clip mask [rows, cols/8])."""
+    R, Cc, ld = _bf16_2d(x)
+    out = _alloc_mx(R, Cc, x.device)
+    m = torch.empty((R, Cc // 8), dtype=torch.uint8, device=x.device)
+    _check(lib().fp4mx_quest_quantize(_ptr(x), R, Cc, ld, float(clip), mask, _ptr(out.codes),
+                                      _ptr(out.scales), _ptr(m), _stream(x.device)))
+    return out, m
+
+
+def requantize(a: MXTensor, rounding=SR, mask=0, seed=0, rng_stream=0) -> MXTensor:
+    """Dequantize an MXFP4 operand [rows, cols], transpose, RHT along rows and
+    quantize again: the operand [cols, rows]."""
+    rows, cols = a.codes.shape[0], a.codes.shape[1] * 2
+    out = _alloc_mx(cols, rows, a.codes.device)
+    _check(lib().fp4mx_requantize(_ptr(a.codes), _ptr(a.scales), rows, cols, rounding, mask, int(seed),
+                                  rng_stream, _ptr(out.codes), _ptr(out.scales),
+                                  _stream(a.codes.device)))
+    return out
+
+
+def unmask_inverse_hadamard(c, clip_mask, mask=0):
+    """In place: c <- H^-1(c with clipped entries zeroed), per 32-group along rows."""
+    if c.dtype != torch.float32 or c.dim() != 2 or c.stride(1) != 1:
+        raise ValueError("c must be a row-major fp32 matrix")
+    _check(lib().fp4mx_unmask_inverse_hadamard(_ptr(c), c.shape[0], c.shape[1], c.stride(0),
+                                               _ptr(clip_mask), mask, _stream(c.device)))
+    return c
+
+
+@dataclass
+class QuestCtx:
+    xq: MXTensor
+    wq: MXTensor
+    x_mask: torch.Tensor
+    w_mask: torch.Tensor
+    seed: int
+
+    def as_struct(self):
+        return QuestCtxStruct(self.xq.codes.data_ptr(), self.xq.scales.data_ptr(),
+                              self.wq.codes.data_ptr(), self.wq.scales.data_ptr(),
+                              self.x_mask.data_ptr(), self.w_mask.data_ptr(), self.seed)
+
+
+def quest_linear_fwd(x, w, seed=0, clip=QUEST_CLIP, ctx=None, out=None):
+    """Y = X_q W_q^T with QuEST operands; returns (Y fp32, QuestCtx)."""
+    m, k, _ = _bf16_2d(x)
+    n, k2, _ = _bf16_2d(w)
+    if k2 != k or not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("x [m,k], w [n,k] contiguous")
+    dev = x.device
+    if ctx is None:
+        ctx = QuestCtx(_alloc_mx(m, k, dev), _alloc_mx(n, k, dev),
+                       torch.empty((m, k // 8), dtype=torch.uint8, device=dev),
+                       torch.empty((n, k // 8), dtype=torch.uint8, device=dev), seed)
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    st = ctx.as_struct()
+    _check(lib().fp4mx_quest_linear_fwd(_ptr(x), _ptr(w), m, n, k, float(clip), seed, _ptr(y),
+                                        C.byref(st), _stream(dev)))
+    return y, ctx
+
+
+def quest_linear_bwd(dy, ctx: QuestCtx, ws=None, dx=None, dw=None):
+    """dX, dW in the forward-rotated basis with mask correction and inverse RHT (fp32)."""
+    m, n, _ = _bf16_2d(dy)
+    k = ctx.xq.codes.shape[1] * 2
+    if not dy.is_contiguous():
+        raise ValueError("dy must be contiguous")
+    dev = dy.device
+    if ws is None:
+        ws = torch.empty(lib().fp4mx_quest_bwd_workspace_bytes(m, n, k), dtype=torch.uint8, device=dev)
+    dx = dx if dx is not None else torch.empty((m, k), dtype=torch.float32, device=dev)
+    dw = dw if dw is not None else torch.empty((n, k), dtype=torch.float32, device=dev)
+    st = ctx.as_struct()
+    _check(lib().fp4mx_quest_linear_bwd(_ptr(dy), C.byref(st), m, n, k, _ptr(dx), _ptr(dw), _ptr(ws),
+                                        ws.numel(), _stream(dev)))
     return dx, dw
 
 

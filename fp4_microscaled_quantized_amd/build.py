@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp4mx.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["quant_mx.hip", "gemm_mx.hip", "nvfp4.hip", "msedn.hip", "abi.hip"]
+SOURCES = ["quant_mx.hip", "gemm_mx.hip", "nvfp4.hip", "msedn.hip", "quest.hip", "abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -50,7 +50,7 @@ def _compile(src: str) -> str:
 
 def build_library(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs

@@ -245,6 +245,136 @@ int fp4mx_linear_bwd(const void* dy, const fp4mx_ctx* ctx, int64_t m, int64_t n,
   return e == hipSuccess ? FP4MX_OK : hip_fail(e);
 }
 
+// ------------------------------- QuEST -------------------------------------
+
+static bool clip_ok(float c) { return c > 0.0f && c <= 3.0e38f; }
+static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int fp4mx_quest_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, float clip,
+                         uint32_t sign_mask, uint8_t* codes, uint8_t* scales, uint8_t* mask,
+                         void* stream) {
+  int st = check_quant_args(x, rows, cols, ld, FP4MX_ROUND_RTN, codes, scales);
+  if (st) return st;
+  if (!mask) return FP4MX_E_NULL;
+  if (!aligned4(mask)) return FP4MX_E_ALIGN;
+  if (!clip_ok(clip)) return FP4MX_E_ARG;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_quest_row(static_cast<const uint16_t*>(x), rows, cols, ld, sign_mask, clip,
+                                  codes, scales, mask, (hipStream_t)stream);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+int fp4mx_requantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                     int rounding, uint32_t sign_mask, uint64_t seed, uint32_t rng_stream,
+                     uint8_t* out_codes, uint8_t* out_scales, void* stream) {
+  if (!codes || !scales || !out_codes || !out_scales) return FP4MX_E_NULL;
+  if (!dim_ok(rows) || !dim_ok(cols)) return FP4MX_E_SHAPE;
+  if (!aligned16(codes) || !aligned16(out_codes)) return FP4MX_E_ALIGN;
+  if (rounding != FP4MX_ROUND_RTN && rounding != FP4MX_ROUND_SR) return FP4MX_E_ARG;
+  int st = check_device();
+  if (st) return st;
+  hipError_t e = launch_requant(codes, scales, rows, cols, rounding, sign_mask,
+                                make_key(seed, rng_stream), out_codes, out_scales,
+                                (hipStream_t)stream);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+int fp4mx_unmask_inverse_hadamard(float* c, int64_t rows, int64_t cols, int64_t ldc,
+                                  const uint8_t* mask, uint32_t sign_mask, void* stream) {
+  if (!c || !mask) return FP4MX_E_NULL;
+  if (!dim_ok(rows) || !dim_ok(cols) || ldc < cols) return FP4MX_E_SHAPE;
+  if (!aligned16(c) || ldc % 4 != 0 || !aligned4(mask)) return FP4MX_E_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  hipError_t e = launch_unmask_irht(c, rows, cols, ldc, mask, sign_mask, (hipStream_t)stream);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+size_t fp4mx_quest_ctx_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
+  return mx_bytes(m, k) + mx_bytes(n, k) + round_up((size_t)m * k / 8) + round_up((size_t)n * k / 8);
+}
+
+size_t fp4mx_quest_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
+  return 2 * mx_bytes(m, n) + mx_bytes(k, n) + mx_bytes(k, m);
+}
+
+static int quest_ctx_check(const fp4mx_quest_ctx* ctx) {
+  if (!ctx) return FP4MX_E_NULL;
+  if (!ctx->xq_codes || !ctx->xq_scales || !ctx->wq_codes || !ctx->wq_scales || !ctx->x_mask ||
+      !ctx->w_mask)
+    return FP4MX_E_NULL;
+  if (!aligned16(ctx->xq_codes) || !aligned16(ctx->wq_codes) || !aligned4(ctx->x_mask) ||
+      !aligned4(ctx->w_mask))
+    return FP4MX_E_ALIGN;
+  return FP4MX_OK;
+}
+
+int fp4mx_quest_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t k,
+                           float clip, uint64_t seed, float* y, const fp4mx_quest_ctx* ctx,
+                           void* stream) {
+  if (!x || !w || !y) return FP4MX_E_NULL;
+  int st = quest_ctx_check(ctx);
+  if (st) return st;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return FP4MX_E_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return FP4MX_E_ALIGN;
+  if (!clip_ok(clip) || ctx->seed != seed) return FP4MX_E_ARG;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const uint32_t g0 = fp4mx_sign_mask(seed, 0);
+  hipError_t e = launch_quest_row(static_cast<const uint16_t*>(x), m, k, k, g0, clip,
+                                  ctx->xq_codes, ctx->xq_scales, ctx->x_mask, s);
+  if (e == hipSuccess)
+    e = launch_quest_row(static_cast<const uint16_t*>(w), n, k, k, g0, clip, ctx->wq_codes,
+                         ctx->wq_scales, ctx->w_mask, s);
+  if (e == hipSuccess)
+    e = launch_mx_gemm(ctx->xq_codes, ctx->xq_scales, ctx->wq_codes, ctx->wq_scales, m, n, k, 1.0f,
+                       y, n, s);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+int fp4mx_quest_linear_bwd(const void* dy, const fp4mx_quest_ctx* ctx, int64_t m, int64_t n,
+                           int64_t k, float* dx, float* dw, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!dy || !dx || !dw) return FP4MX_E_NULL;
+  int st = quest_ctx_check(ctx);
+  if (st) return st;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return FP4MX_E_SHAPE;
+  if (!aligned16(dy) || !aligned16(dx) || !aligned16(dw)) return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4mx_quest_bwd_workspace_bytes(m, n, k)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const uint64_t seed = ctx->seed;
+  const uint32_t g0 = fp4mx_sign_mask(seed, 0), g1 = fp4mx_sign_mask(seed, 1),
+                 g2 = fp4mx_sign_mask(seed, 2);
+  Carver cv{static_cast<uint8_t*>(ws)};
+  uint8_t* dq = cv.take((size_t)m * n / 2);
+  uint8_t* ds = cv.take((size_t)m * n / 32);
+  uint8_t* tq = cv.take((size_t)n * m / 2);
+  uint8_t* ts = cv.take((size_t)n * m / 32);
+  uint8_t* wtq = cv.take((size_t)k * n / 2);
+  uint8_t* wts = cv.take((size_t)k * n / 32);
+  uint8_t* xtq = cv.take((size_t)k * m / 2);
+  uint8_t* xts = cv.take((size_t)k * m / 32);
+  QuantOut r{FP4MX_ROUND_SR, g1, make_key(seed, 1), dq, ds};
+  QuantOut c{FP4MX_ROUND_SR, g2, make_key(seed, 3), tq, ts};
+  const float alpha = 16.0f / 9.0f;
+  hipError_t e = launch_quant_tile(static_cast<const uint16_t*>(dy), m, n, n, true, &r, &c, s);
+  if (e == hipSuccess)
+    e = launch_requant(ctx->wq_codes, ctx->wq_scales, n, k, FP4MX_ROUND_SR, g1, make_key(seed, 2),
+                       wtq, wts, s);
+  if (e == hipSuccess)
+    e = launch_requant(ctx->xq_codes, ctx->xq_scales, m, k, FP4MX_ROUND_SR, g2, make_key(seed, 4),
+                       xtq, xts, s);
+  if (e == hipSuccess) e = launch_mx_gemm(dq, ds, wtq, wts, m, k, n, alpha, dx, k, s);
+  if (e == hipSuccess) e = launch_unmask_irht(dx, m, k, k, ctx->x_mask, g0, s);
+  if (e == hipSuccess) e = launch_mx_gemm(tq, ts, xtq, xts, n, k, m, alpha, dw, k, s);
+  if (e == hipSuccess) e = launch_unmask_irht(dw, n, k, k, ctx->w_mask, g0, s);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
 // ------------------------------- NVFP4 -------------------------------------
 
 size_t fp4nv_quantize_workspace_bytes(int64_t rows, int64_t cols) {

@@ -66,6 +66,16 @@ hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                           const uint8_t* bs, int64_t m, int64_t n, int64_t k, float alpha,
                           float* c, int64_t ldc, hipStream_t s);
 
+// QuEST and the re-quantizer (csrc/quest.hip).
+hipError_t launch_quest_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                            uint32_t sign_mask, float clip, uint8_t* codes, uint8_t* scales,
+                            uint8_t* mask, hipStream_t s);
+hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                          int rounding, uint32_t sign_mask, RngKey key, uint8_t* out_codes,
+                          uint8_t* out_scales, hipStream_t s);
+hipError_t launch_unmask_irht(float* c, int64_t rows, int64_t cols, int64_t ldc,
+                              const uint8_t* mask, uint32_t sign_mask, hipStream_t s);
+
 // MS-EDEN, two passes (csrc/msedn.hip).  vbuf: fp32 per output 16-group;
 // gmax: one uint32 (global max of vbuf).
 hipError_t launch_msedn(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int axis,

@@ -191,6 +191,80 @@ FP4MX_API int fp4mx_linear_bwd(const void* dy, const fp4mx_ctx* ctx, int64_t m, 
                      void* stream);
 
 /* ------------------------------------------------------------------------
+ * QuEST forward and the Quartet backward in the forward-rotated basis
+ * (source: "Quartet: Native FP4 Training Can Be Optimal for Large Language
+ * Models" -- "The Forward-Pass Quantization: QuEST in Detail", Stage 1 of
+ * "The GPU Kernel Implementation", the inverse Hadamard and clipping-mask
+ * correction, "The Complete Quartet Algorithm").
+ * Clipping masks: uint8 [rows][cols/8], element j of a row at bit j%8 of byte
+ * j/8; bit 1 = the element was clipped.  Mask pointers must be 4-B aligned.
+ * ------------------------------------------------------------------------ */
+
+/* QuEST MXFP4 quantization along rows after the block-32 RHT (sign_mask):
+ * per 32-group, sigma = standard deviation about the group mean (evaluated on
+ * the group scaled by 2^-E, 2^E <= max|y| < 2^(E+1)), T = clip * sigma, E8M0
+ * scale floor(log2 T) - 2 (0 when T = 0), codes = E2M1 RNE of the group
+ * clamped to [-T, T], mask bit = |y| > T.  A non-finite group gets scale 0xFF,
+ * codes 0 and mask 0.  clip must be finite and > 0; the Gaussian RMSE
+ * optimum of the page's objective is 2.922475.
+ *   x bf16 [rows][ld]; codes [rows][cols/2]; scales [rows][cols/32];
+ *   mask [rows][cols/8].  Errors as fp4mx_quantize; E_ARG for a bad clip. */
+FP4MX_API int fp4mx_quest_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, float clip,
+                         uint32_t sign_mask, uint8_t* codes, uint8_t* scales, uint8_t* mask,
+                         void* stream);
+
+/* Re-quantize a saved MXFP4 operand for the backward pass: dequantize A
+ * [rows][cols] (codes [rows][cols/2], scales [rows][cols/32], groups along
+ * cols), transpose, apply the block-32 RHT (sign_mask) along rows and quantize
+ * with `rounding` (SR includes the 3/4 prescale): out_codes [cols][rows/2],
+ * out_scales [cols][rows/32].  SR draw of output element (r, c): index
+ * r * rows + c of stream rng_stream.  Dequantized values are exact (0xFF
+ * scales give NaN groups -> 0xFF).  Errors as fp4mx_quantize. */
+FP4MX_API int fp4mx_requantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                     int rounding, uint32_t sign_mask, uint64_t seed, uint32_t rng_stream,
+                     uint8_t* out_codes, uint8_t* out_scales, void* stream);
+
+/* In place on fp32 c [rows][ldc] (first cols columns): per 32-group along each
+ * row, zero the entries whose mask bit is 1, then apply the inverse of the
+ * forward RHT, x = s o (fl32(1/sqrt(32)) * FWHT(y)).  ldc multiple of 4. */
+FP4MX_API int fp4mx_unmask_inverse_hadamard(float* c, int64_t rows, int64_t cols, int64_t ldc,
+                                  const uint8_t* mask, uint32_t sign_mask, void* stream);
+
+/* Saved QuEST forward context: X_q [m][k] (codes, scales), W_q [n][k], the
+ * clipping masks M_x [m][k/8] and M_w [n][k/8], and the seed.  Caller-owned
+ * device memory; fp4mx_quest_ctx_bytes gives the total of the six buffers. */
+typedef struct {
+  uint8_t* xq_codes;
+  uint8_t* xq_scales;
+  uint8_t* wq_codes;
+  uint8_t* wq_scales;
+  uint8_t* x_mask;
+  uint8_t* w_mask;
+  uint64_t seed;
+} fp4mx_quest_ctx;
+
+FP4MX_API size_t fp4mx_quest_ctx_bytes(int64_t m, int64_t n, int64_t k);
+/* Workspace of fp4mx_quest_linear_bwd: Q(dY), Q(dY^T), Q(W_q^T), Q(X_q^T). */
+FP4MX_API size_t fp4mx_quest_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* Forward: X_q, M_x = QuEST(RHT X), W_q, M_w = QuEST(RHT W) along k with
+ * fp4mx_sign_mask(seed, 0), written into ctx (required, ctx->seed == seed);
+ * y fp32 [m][n] = X_q W_q^T. */
+FP4MX_API int fp4mx_quest_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t k,
+                           float clip, uint64_t seed, float* y, const fp4mx_quest_ctx* ctx,
+                           void* stream);
+
+/* Backward in the forward-rotated basis:
+ *   dX = 16/9 H^-1(Q(dY) Q(W_q^T)^T with M_x entries zeroed)  [m][k],
+ *   dW = 16/9 H^-1(Q(dY^T) Q(X_q^T)^T with M_w entries zeroed) [n][k];
+ * Q(dY): rows SR, mask fp4mx_sign_mask(seed, 1), stream 1; Q(dY^T): SR, mask
+ * 2, stream 3; W_q re-quantized along n (mask 1, stream 2); X_q along m (mask
+ * 2, stream 4); H^-1 inverts the forward rotation (mask 0). */
+FP4MX_API int fp4mx_quest_linear_bwd(const void* dy, const fp4mx_quest_ctx* ctx, int64_t m, int64_t n,
+                           int64_t k, float* dx, float* dw, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
  * NVFP4 forward variant (sources: "Quartet II ..." -- "NVFP4 Format and
  * Standard Stochastic Rounding", "MS-EDEN" Step 2 (global scale amax/(s*256)),
  * "Forward Pass Design: ... Four-Over-Six").

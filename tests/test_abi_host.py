@@ -103,3 +103,29 @@ def test_product_path_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError):
         binding.lib()
+
+
+def test_quest_validation():
+    L = binding.lib()
+    keep, p = _buf()
+    f = C.c_void_p(p.value)
+    m4 = C.c_void_p(p.value + 4)
+    assert L.fp4mx_quest_quantize(p, 64, 64, 64, 2.9, 0, p, p, None, None) == -1
+    assert L.fp4mx_quest_quantize(p, 64, 64, 64, 2.9, 0, p, p, C.c_void_p(p.value + 2), None) == -3
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert L.fp4mx_quest_quantize(p, 64, 64, 64, bad, 0, p, p, m4, None) == -4
+    assert L.fp4mx_quest_quantize(p, 64, 48, 64, 2.9, 0, p, p, m4, None) == -2
+    assert L.fp4mx_requantize(p, p, 64, 40, 1, 0, 0, 0, p, p, None) == -2
+    assert L.fp4mx_requantize(p, p, 64, 64, 2, 0, 0, 0, p, p, None) == -4
+    assert L.fp4mx_requantize(None, p, 64, 64, 1, 0, 0, 0, p, p, None) == -1
+    assert L.fp4mx_unmask_inverse_hadamard(f, 64, 64, 62, p, 0, None) == -2
+    assert L.fp4mx_unmask_inverse_hadamard(f, 64, 64, 66, p, 0, None) == -3
+    ctx = binding.QuestCtxStruct(p.value, p.value, p.value, p.value, p.value, p.value, 3)
+    assert L.fp4mx_quest_linear_fwd(p, p, 64, 64, 64, 2.9, 4, f, C.byref(ctx), None) == -4
+    assert L.fp4mx_quest_linear_fwd(p, p, 64, 64, 64, 2.9, 3, f, None, None) == -1
+    assert L.fp4mx_quest_linear_bwd(p, C.byref(ctx), 64, 64, 64, f, f, p, 16, None) == -5
+    bad = binding.QuestCtxStruct(p.value, p.value, p.value, p.value, p.value + 1, p.value, 3)
+    assert L.fp4mx_quest_linear_bwd(p, C.byref(bad), 64, 64, 64, f, f, p, 1 << 20, None) == -3
+    m, n, k = 8192, 4096, 4096
+    assert L.fp4mx_quest_ctx_bytes(m, n, k) == (m * k + n * k) * 17 // 32 + (m * k + n * k) // 8
+    assert L.fp4mx_quest_bwd_workspace_bytes(m, n, k) == (2 * m * n + k * n + k * m) * 17 // 32
