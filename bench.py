@@ -57,7 +57,48 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-class LinearStep:
+class _Step:
+    """A sequence of C-ABI launches on one stream, timed per step and per launch."""
+
+    def run(self, steps, timed):
+        """`steps` passes of the launches, back to back; when timed, one event
+        per step boundary (no events between the kernels of a step)."""
+        import torch
+        calls = self._calls()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)] if timed else None
+        if timed:
+            evs[0].record()
+        for i in range(steps):
+            for c in calls:
+                c()
+            if timed:
+                evs[i + 1].record()
+        return evs
+
+    def kernel_times(self, steps):
+        """In-step duration of each launch: the same steps again with an event
+        after every launch, all on the stream the kernels run on (an event
+        record adds a few microseconds to the launch it follows)."""
+        import torch
+        calls = self._calls()
+        evs = []
+        for _ in range(steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+            ev[0].record()
+            for i, c in enumerate(calls):
+                c()
+                ev[i + 1].record()
+            evs.append(ev)
+        torch.cuda.synchronize()
+        for ev in evs:
+            for i, nm in enumerate(self.names):
+                self.times[nm].append(ev[i].elapsed_time(ev[i + 1]))
+
+    def flops(self):
+        return 6.0 * self.m * self.n * self.k
+
+
+class LinearStep(_Step):
     """The MXFP4 linear fwd+bwd hot path as six C-ABI launches on one stream."""
 
     def __init__(self, d, seed=0):
@@ -105,40 +146,6 @@ class LinearStep:
                                         16.0 / 9.0, _ptr(self.dw), k, s)),
         ]
 
-    def run(self, steps, timed):
-        """`steps` passes of the six launches, back to back; when timed, one
-        event per step boundary (no events between the kernels of a step)."""
-        import torch
-        calls = self._calls()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)] if timed else None
-        if timed:
-            evs[0].record()
-        for i in range(steps):
-            for c in calls:
-                c()
-            if timed:
-                evs[i + 1].record()
-        return evs
-
-    def kernel_times(self, steps):
-        """In-step duration of each launch: the same steps again with an event
-        after every launch, all on the stream the kernels run on (an event
-        record adds a few microseconds to the launch it follows)."""
-        import torch
-        calls = self._calls()
-        evs = []
-        for _ in range(steps):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-            ev[0].record()
-            for i, c in enumerate(calls):
-                c()
-                ev[i + 1].record()
-            evs.append(ev)
-        torch.cuda.synchronize()
-        for ev in evs:
-            for i, nm in enumerate(self.names):
-                self.times[nm].append(ev[i].elapsed_time(ev[i + 1]))
-
     def check_against_composite(self):
         """The decomposed calls must reproduce fp4mx_linear_fwd / _bwd bit for bit."""
         import torch
@@ -152,13 +159,82 @@ class LinearStep:
         if not ok:
             raise SystemExit("decomposed step differs from fp4mx_linear_fwd/bwd")
 
-    def flops(self):
-        return 6.0 * self.m * self.n * self.k
 
 
-def time_linear(d, steps, warmup, seed=0):
+class QuestStep(_Step):
+    """QuEST forward + the Quartet backward in the forward-rotated basis as ten
+    C-ABI launches: QuEST X, QuEST W, GEMM Y, dual SR quant dY, re-quantize
+    W_q and X_q, GEMM dX, mask + inverse RHT dX, GEMM dW, mask + inverse RHT dW."""
+
+    def __init__(self, d, seed=0):
+        import torch
+        import fp4_microscaled_quantized_amd as fq
+        self.fq = fq
+        self.x, self.w, self.dy = dev_bf16(d["x"]), dev_bf16(d["w"]), dev_bf16(d["dy"])
+        self.m, self.k = self.x.shape
+        self.n = self.w.shape[0]
+        self.seed = seed
+        m, n, k = self.m, self.n, self.k
+        dev = self.x.device
+        e = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+        self.xq, self.xs, self.xm = e(m, k // 2), e(m, k // 32), e(m, k // 8)
+        self.wq, self.wsc, self.wm = e(n, k // 2), e(n, k // 32), e(n, k // 8)
+        self.xtq, self.xts, self.wtq, self.wts = e(k, m // 2), e(k, m // 32), e(k, n // 2), e(k, n // 32)
+        self.dq, self.ds, self.dtq, self.dts = e(m, n // 2), e(m, n // 32), e(n, m // 2), e(n, m // 32)
+        f = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+        self.y, self.dx, self.dw = f(m, n), f(m, k), f(n, k)
+        self.g = [fq.sign_mask(seed, i) for i in range(3)]
+        self.names = ["quest_x", "quest_w", "gemm_y", "quant_dy", "requant_w", "requant_x", "gemm_dx",
+                      "unmask_dx", "gemm_dw", "unmask_dw"]
+        self.times = {nm: [] for nm in self.names}
+
+    def _calls(self):
+        fq, L = self.fq, self.fq.lib()
+        from fp4_microscaled_quantized_amd.binding import _check, _ptr, _stream
+        s = _stream()
+        m, n, k, seed = self.m, self.n, self.k, self.seed
+        g0, g1, g2 = self.g
+        c = float(fq.QUEST_CLIP)
+        SR = fq.SR
+        a = 16.0 / 9.0
+        return [
+            lambda: _check(L.fp4mx_quest_quantize(_ptr(self.x), m, k, k, c, g0, _ptr(self.xq), _ptr(self.xs),
+                                                  _ptr(self.xm), s)),
+            lambda: _check(L.fp4mx_quest_quantize(_ptr(self.w), n, k, k, c, g0, _ptr(self.wq), _ptr(self.wsc),
+                                                  _ptr(self.wm), s)),
+            lambda: _check(L.fp4mx_gemm(_ptr(self.xq), _ptr(self.xs), _ptr(self.wq), _ptr(self.wsc), m, n, k,
+                                        1.0, _ptr(self.y), n, s)),
+            lambda: _check(L.fp4mx_hadamard_quantize_dual(_ptr(self.dy), m, n, n, SR, g1, 1, SR, g2, 3, seed,
+                                                          _ptr(self.dq), _ptr(self.ds), _ptr(self.dtq),
+                                                          _ptr(self.dts), s)),
+            lambda: _check(L.fp4mx_requantize(_ptr(self.wq), _ptr(self.wsc), n, k, SR, g1, seed, 2,
+                                              _ptr(self.wtq), _ptr(self.wts), s)),
+            lambda: _check(L.fp4mx_requantize(_ptr(self.xq), _ptr(self.xs), m, k, SR, g2, seed, 4,
+                                              _ptr(self.xtq), _ptr(self.xts), s)),
+            lambda: _check(L.fp4mx_gemm(_ptr(self.dq), _ptr(self.ds), _ptr(self.wtq), _ptr(self.wts), m, k, n,
+                                        a, _ptr(self.dx), k, s)),
+            lambda: _check(L.fp4mx_unmask_inverse_hadamard(_ptr(self.dx), m, k, k, _ptr(self.xm), g0, s)),
+            lambda: _check(L.fp4mx_gemm(_ptr(self.dtq), _ptr(self.dts), _ptr(self.xtq), _ptr(self.xts), n, k, m,
+                                        a, _ptr(self.dw), k, s)),
+            lambda: _check(L.fp4mx_unmask_inverse_hadamard(_ptr(self.dw), n, k, k, _ptr(self.wm), g0, s)),
+        ]
+
+    def check_against_composite(self):
+        """The decomposed calls must reproduce fp4mx_quest_linear_fwd / _bwd bit for bit."""
+        import torch
+        fq = self.fq
+        self.run(1, False)
+        y, ctx = fq.quest_linear_fwd(self.x, self.w, seed=self.seed)
+        dx, dw = fq.quest_linear_bwd(self.dy, ctx)
+        torch.cuda.synchronize()
+        ok = (torch.equal(y, self.y) and torch.equal(dx, self.dx) and torch.equal(dw, self.dw)
+              and torch.equal(ctx.x_mask, self.xm) and torch.equal(ctx.wq.scales, self.wsc))
+        if not ok:
+            raise SystemExit("decomposed QuEST step differs from fp4mx_quest_linear_fwd/bwd")
+
+
+def time_step(st, steps, warmup):
     import torch
-    st = LinearStep(d, seed)
     st.check_against_composite()
     st.run(warmup, False)
     torch.cuda.synchronize()
@@ -169,6 +245,33 @@ def time_linear(d, steps, warmup, seed=0):
     step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     st.kernel_times(steps)
     avg = {nm: float(np.mean(v)) for nm, v in st.times.items()}
+    return wall, avg, step_ms
+
+
+def time_quest(steps, warmup):
+    """The QuEST layer on the Quartet workload: step rate and each kernel
+    against its roofline (algorithmic bytes: QuEST 2 + 0.5 + 1/32 + 1/8 B per
+    element, re-quantizer 2 x 0.53125, mask + inverse RHT 4 + 1/8 + 4)."""
+    from fp4_microscaled_quantized_amd import synth
+    st = QuestStep(synth.quartet_linear(0))
+    wall, avg, _ = time_step(st, steps, warmup)
+    ms = wall * 1e3 / steps
+    m, n, k = st.m, st.n, st.k
+    by = {"quest_x": m * k * (2 + 0.5 + 1 / 32 + 1 / 8), "quest_w": n * k * (2 + 0.5 + 1 / 32 + 1 / 8),
+          "requant_w": n * k * 2 * (0.5 + 1 / 32), "requant_x": m * k * 2 * (0.5 + 1 / 32),
+          "unmask_dx": m * k * (8 + 1 / 8), "unmask_dw": n * k * (8 + 1 / 8)}
+    kr = {nm: {"GB/s": round(b / (avg[nm] * 1e-3) / 1e9, 1),
+               "frac_hbm": round(b / (avg[nm] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)} for nm, b in by.items()}
+    gemm_ms = avg["gemm_y"] + avg["gemm_dx"] + avg["gemm_dw"]
+    return {"workload": "QuEST fwd + Quartet bwd (rotated basis, masks, inverse RHT) M=8192 N=K=4096",
+            "ms_per_step": round(ms, 4), "TFLOP/s": round(st.flops() / (ms * 1e-3) / 1e12, 1),
+            "gemm_TFLOP/s": round(6.0 * m * n * k / (gemm_ms * 1e-3) / 1e12, 1),
+            "breakdown_ms": {nm: round(v, 4) for nm, v in avg.items()}, "kernel_hbm": kr}
+
+
+def time_linear(d, steps, warmup, seed=0):
+    st = LinearStep(d, seed)
+    wall, avg, step_ms = time_step(st, steps, warmup)
     return st, wall, avg, step_ms
 
 
@@ -421,6 +524,8 @@ def main():
         out["nvfp4"] = time_nvfp4(max(a.steps // 2, 5), 2)
         torch.cuda.empty_cache()
         out["nvfp4_bwd_ms_eden"] = time_nvfp4_bwd(max(a.steps // 2, 5), 2)
+        torch.cuda.empty_cache()
+        out["quest_linear"] = time_quest(a.steps, a.warmup)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
