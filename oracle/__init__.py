@@ -28,9 +28,12 @@ QuEST (the Gaussian objective against quadrature and Monte Carlo, its
 minimum, sigma and thresholds against fp64, reduction of clipping groups to MX
 RTN, the page's MSE ranking QuEST < RTN < SR, power-of-two invariance) and the
 Quartet backward in the rotated basis (inverse RHT against the matrix
-inverse, mask correction, re-quantization and the whole backward unbiased).
+inverse, mask correction, re-quantization and the whole backward unbiased),
+and the Quartet II graph with re-quantized saved NVFP4 operands (de-quantization
+as the rounded exact product, Table 1's MS-EDEN error on re-quantized
+operands, unbiased backward).
 Parity unpinned: the FP8 staging of the NVFP4 GEMM (a design of this library
 that the pages do not describe; only its self-consistency is checked).
 """
 
-from . import formats, rng, rht, mx, nvfp4, msedn, quest  # noqa: F401
+from . import formats, rng, rht, mx, nvfp4, msedn, quest, quartet2  # noqa: F401
