@@ -6,6 +6,7 @@ in ``include/fp4mx.h``); ``binding`` is its thin ctypes wrapper.
 """
 from .binding import (COL, QUEST_CLIP, ROW, RTN, SR, FP4LinearFunction, LinearCtx, MXTensor, NVTensor,  # noqa: F401
                       gemm, hadamard_quantize, hadamard_quantize_dual, lib, linear_bwd, linear_fwd,
-                      nv_gemm, nv_linear_bwd, nv_linear_fwd, nv_msedn_quantize, nv_quantize46, nv_sr_quantize, quantize,
+                      nv_gemm, nv_linear_bwd, nv_linear_bwd_ctx, nv_linear_fwd, nv_linear_fwd_ctx, nv_msedn_quantize,
+                      nv_msedn_requantize, NvCtx, nv_quantize46, nv_sr_quantize, quantize,
                       quest_linear_bwd, quest_linear_fwd, quest_quantize, QuestCtx, requantize, sign_mask,
                       unmask_inverse_hadamard)

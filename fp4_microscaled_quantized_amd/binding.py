@@ -41,6 +41,11 @@ class QuestCtxStruct(C.Structure):
                 ("x_mask", _P), ("w_mask", _P), ("seed", _U64)]
 
 
+class NvCtxStruct(C.Structure):
+    _fields_ = [("xq_codes", _P), ("xq_scales", _P), ("xq_tensor_scale", _P), ("wq_codes", _P),
+                ("wq_scales", _P), ("wq_tensor_scale", _P), ("seed", _U64)]
+
+
 _SIGS = {
     "fp4mx_status_string": (C.c_char_p, [_INT]),
     "fp4mx_last_hip_error": (_INT, []),
@@ -75,6 +80,12 @@ _SIGS = {
                                     _P, _P, _P, _SZ, _P]),
     "fp4nv_linear_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4nv_linear_bwd": (_INT, [_P, _P, _P, _I64, _I64, _I64, _U64, _P, _P, _P, _SZ, _P]),
+    "fp4nv_msedn_requantize": (_INT, [_P, _P, _P, _I64, _I64, C.c_float, _U64, _U32, _U32, _P, _P, _P,
+                                      _P, _P, _SZ, _P]),
+    "fp4nv_ctx_bytes": (_SZ, [_I64, _I64, _I64]),
+    "fp4nv_linear_fwd_ctx_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "fp4nv_linear_fwd_ctx": (_INT, [_P, _P, _I64, _I64, _I64, _P, C.POINTER(NvCtxStruct), _P, _SZ, _P]),
+    "fp4nv_linear_bwd_ctx": (_INT, [_P, C.POINTER(NvCtxStruct), _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -400,6 +411,71 @@ def nv_linear_bwd(dy, x, w, seed=0, ws=None, dx=None, dw=None):
     dw = dw if dw is not None else torch.empty((n, k), dtype=torch.float32, device=dev)
     _check(lib().fp4nv_linear_bwd(_ptr(dy), _ptr(x), _ptr(w), m, n, k, int(seed), _ptr(dx), _ptr(dw),
                                   _ptr(ws), ws.numel(), _stream(dev)))
+    return dx, dw
+
+
+def nv_msedn_requantize(a: "NVTensor", seed=0, gemm_id=1, stream=6, clip=6.0, want_s=False):
+    """MS-EDEN of the transpose of a saved NVFP4 operand [rows, cols] -> [cols, rows]."""
+    rows, cols = a.codes.shape[0], a.codes.shape[1] * 2
+    dev = a.codes.device
+    out = NVTensor(torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((cols, rows // 16), dtype=torch.uint8, device=dev),
+                   torch.empty(1, dtype=torch.float32, device=dev))
+    s_out = torch.empty((cols, rows // 128), dtype=torch.float32, device=dev) if want_s else None
+    ws = torch.empty(lib().fp4nv_msedn_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
+    _check(lib().fp4nv_msedn_requantize(_ptr(a.codes), _ptr(a.scales), _ptr(a.tensor_scale), rows, cols,
+                                        float(clip), int(seed), gemm_id, stream, _ptr(out.codes),
+                                        _ptr(out.scales), _ptr(out.tensor_scale),
+                                        _ptr(s_out) if want_s else None, _ptr(ws), ws.numel(), _stream(dev)))
+    return (out, s_out) if want_s else out
+
+
+@dataclass
+class NvCtx:
+    """Saved forward operands of the NVFP4 layer and the backward seed."""
+    xq: "NVTensor"
+    wq: "NVTensor"
+    seed: int
+
+    def as_struct(self):
+        return NvCtxStruct(self.xq.codes.data_ptr(), self.xq.scales.data_ptr(),
+                           self.xq.tensor_scale.data_ptr(), self.wq.codes.data_ptr(),
+                           self.wq.scales.data_ptr(), self.wq.tensor_scale.data_ptr(), self.seed)
+
+
+def _alloc_nv(rows, cols, dev):
+    return NVTensor(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+                    torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+                    torch.empty(1, dtype=torch.float32, device=dev))
+
+
+def nv_linear_fwd_ctx(x, w, seed=0, ws=None, out=None):
+    """NVFP4 forward (RTN + 4/6) keeping Q(X), Q(W): (Y fp32, NvCtx)."""
+    m, k, _ = _bf16_2d(x)
+    n, _, _ = _bf16_2d(w)
+    dev = x.device
+    ctx = NvCtx(_alloc_nv(m, k, dev), _alloc_nv(n, k, dev), seed)
+    if ws is None:
+        ws = torch.empty(lib().fp4nv_linear_fwd_ctx_workspace_bytes(m, n, k), dtype=torch.uint8, device=dev)
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    st = ctx.as_struct()
+    _check(lib().fp4nv_linear_fwd_ctx(_ptr(x), _ptr(w), m, n, k, _ptr(y), C.byref(st), _ptr(ws), ws.numel(),
+                                      _stream(dev)))
+    return y, ctx
+
+
+def nv_linear_bwd_ctx(dy, ctx: NvCtx, ws=None, dx=None, dw=None):
+    """NVFP4 backward re-quantizing the saved Q(X), Q(W) with MS-EDEN: (dX, dW) fp32."""
+    m, n, _ = _bf16_2d(dy)
+    k = ctx.xq.codes.shape[1] * 2
+    dev = dy.device
+    if ws is None:
+        ws = torch.empty(lib().fp4nv_linear_bwd_workspace_bytes(m, n, k), dtype=torch.uint8, device=dev)
+    dx = dx if dx is not None else torch.empty((m, k), dtype=torch.float32, device=dev)
+    dw = dw if dw is not None else torch.empty((n, k), dtype=torch.float32, device=dev)
+    st = ctx.as_struct()
+    _check(lib().fp4nv_linear_bwd_ctx(_ptr(dy), C.byref(st), m, n, k, _ptr(dx), _ptr(dw), _ptr(ws),
+                                      ws.numel(), _stream(dev)))
     return dx, dw
 
 

@@ -543,26 +543,39 @@ size_t fp4nv_linear_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   return std::max(q1, q2) + ms + gs + 512;
 }
 
-int fp4nv_linear_bwd(const void* dy, const void* x, const void* w, int64_t m, int64_t n, int64_t k,
-                     uint64_t seed, float* dx, float* dw, void* ws, size_t ws_bytes, void* stream) {
-  if (!dy || !x || !w || !dx || !dw) return FP4MX_E_NULL;
-  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k) || m % 128 != 0 || n % 128 != 0) return FP4MX_E_SHAPE;
-  if (!aligned16(dy) || !aligned16(x) || !aligned16(w) || !aligned16(dx) || !aligned16(dw))
-    return FP4MX_E_ALIGN;
-  if (!ws || ws_bytes < fp4nv_linear_bwd_workspace_bytes(m, n, k)) return FP4MX_E_WORKSPACE;
-  if (!aligned16(ws)) return FP4MX_E_ALIGN;
-  int st = check_device();
-  if (st) return st;
-  hipStream_t s = (hipStream_t)stream;
+// One backward operand of the NVFP4 layer: from bf16 (column axis, i.e. the
+// transposed operand) or from a saved NVFP4 operand (re-quantized).
+struct NvSrc {
+  const void* bf16;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* g;
+};
+
+static int msedn_operand(const NvSrc& src, int64_t rows, int64_t cols, uint64_t seed,
+                         uint32_t gemm_id, uint32_t stream, uint8_t* codes, uint8_t* scales,
+                         float* ts, uint8_t* ws, hipStream_t s) {
+  if (src.bf16)
+    return msedn_impl(src.bf16, rows, cols, cols, FP4MX_AXIS_COL, 6.0f, seed, gemm_id, stream, codes,
+                      scales, ts, nullptr, ws, s);
+  Carver cv{ws};
+  float* vbuf = reinterpret_cast<float*>(cv.take((size_t)rows * cols / 16 * sizeof(float)));
+  uint32_t* gmax = reinterpret_cast<uint32_t*>(cv.take(4));
+  hipError_t e = launch_msedn_requant(src.codes, src.scales, src.g, rows, cols, 6.0f, seed, gemm_id,
+                                      stream, codes, scales, ts, nullptr, vbuf, gmax, s);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+// dX = gemm(MSEDEN(dY), MSEDEN(W^T)) (inner n), dW = gemm(MSEDEN(dY^T), MSEDEN(X^T)) (inner m).
+static int nv_bwd_impl(const void* dy, const NvSrc& x, const NvSrc& w, int64_t m, int64_t n,
+                       int64_t k, uint64_t seed, float* dx, float* dw, uint8_t* base, hipStream_t s) {
+  int st;
   const float clip = 6.0f;
   const size_t qmax = std::max(nv_operand_bytes(m, n) + nv_operand_bytes(k, n),
                                nv_operand_bytes(n, m) + nv_operand_bytes(k, m));
-  uint8_t* base = static_cast<uint8_t*>(ws);
   uint8_t* ms = base + qmax;
   uint8_t* gws = ms + std::max(fp4nv_msedn_workspace_bytes(m, n),
                                std::max(fp4nv_msedn_workspace_bytes(n, k), fp4nv_msedn_workspace_bytes(m, k)));
-  const uint16_t* dyb = static_cast<const uint16_t*>(dy);
-  // dX = dY W: inner dimension n
   {
     Carver cv{base};
     uint8_t* aq = cv.take((size_t)m * n / 2);
@@ -573,11 +586,9 @@ int fp4nv_linear_bwd(const void* dy, const void* x, const void* w, int64_t m, in
     float* bg = reinterpret_cast<float*>(cv.take(256));
     if ((st = msedn_impl(dy, m, n, n, FP4MX_AXIS_ROW, clip, seed, 1, 5, aq, as, ag, nullptr, ms, s)))
       return st;
-    if ((st = msedn_impl(w, n, k, k, FP4MX_AXIS_COL, clip, seed, 1, 6, bq, bs, bg, nullptr, ms, s)))
-      return st;
+    if ((st = msedn_operand(w, n, k, seed, 1, 6, bq, bs, bg, ms, s))) return st;
     if ((st = nv_gemm_impl(aq, as, ag, bq, bs, bg, m, k, n, dx, k, gws, s))) return st;
   }
-  // dW = dY^T X: inner dimension m
   {
     Carver cv{base};
     uint8_t* aq = cv.take((size_t)n * m / 2);
@@ -586,13 +597,118 @@ int fp4nv_linear_bwd(const void* dy, const void* x, const void* w, int64_t m, in
     uint8_t* bq = cv.take((size_t)k * m / 2);
     uint8_t* bs = cv.take((size_t)k * m / 16);
     float* bg = reinterpret_cast<float*>(cv.take(256));
-    if ((st = msedn_impl(dyb, m, n, n, FP4MX_AXIS_COL, clip, seed, 2, 7, aq, as, ag, nullptr, ms, s)))
+    if ((st = msedn_impl(dy, m, n, n, FP4MX_AXIS_COL, clip, seed, 2, 7, aq, as, ag, nullptr, ms, s)))
       return st;
-    if ((st = msedn_impl(x, m, k, k, FP4MX_AXIS_COL, clip, seed, 2, 8, bq, bs, bg, nullptr, ms, s)))
-      return st;
+    if ((st = msedn_operand(x, m, k, seed, 2, 8, bq, bs, bg, ms, s))) return st;
     if ((st = nv_gemm_impl(aq, as, ag, bq, bs, bg, n, k, m, dw, k, gws, s))) return st;
   }
   return FP4MX_OK;
+}
+
+int fp4nv_linear_bwd(const void* dy, const void* x, const void* w, int64_t m, int64_t n, int64_t k,
+                     uint64_t seed, float* dx, float* dw, void* ws, size_t ws_bytes, void* stream) {
+  if (!dy || !x || !w || !dx || !dw) return FP4MX_E_NULL;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k) || m % 128 != 0 || n % 128 != 0) return FP4MX_E_SHAPE;
+  if (!aligned16(dy) || !aligned16(x) || !aligned16(w) || !aligned16(dx) || !aligned16(dw))
+    return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4nv_linear_bwd_workspace_bytes(m, n, k)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  const NvSrc xs{x, nullptr, nullptr, nullptr}, wsrc{w, nullptr, nullptr, nullptr};
+  return nv_bwd_impl(dy, xs, wsrc, m, n, k, seed, dx, dw, static_cast<uint8_t*>(ws),
+                     (hipStream_t)stream);
+}
+
+int fp4nv_msedn_requantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                           int64_t rows, int64_t cols, float clip_s, uint64_t seed, uint32_t gemm_id,
+                           uint32_t rng_stream, uint8_t* out_codes, uint8_t* out_scales,
+                           float* out_tensor_scale, float* eden_s, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!codes || !scales || !tensor_scale || !out_codes || !out_scales || !out_tensor_scale)
+    return FP4MX_E_NULL;
+  if (!dim_ok(rows) || !dim_ok(cols) || rows % 128 != 0) return FP4MX_E_SHAPE;
+  if (!(clip_s > 0.0f) || !(clip_s < 1e30f)) return FP4MX_E_ARG;
+  if (!aligned16(codes) || ((uintptr_t)scales & 1u) || ((uintptr_t)tensor_scale & 3u) ||
+      !aligned16(out_codes) || ((uintptr_t)out_scales & 1u) || ((uintptr_t)out_tensor_scale & 3u) ||
+      ((uintptr_t)eden_s & 3u))
+    return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4nv_msedn_workspace_bytes(rows, cols)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  Carver cv{static_cast<uint8_t*>(ws)};
+  float* vbuf = reinterpret_cast<float*>(cv.take((size_t)rows * cols / 16 * sizeof(float)));
+  uint32_t* gmax = reinterpret_cast<uint32_t*>(cv.take(4));
+  hipError_t e = launch_msedn_requant(codes, scales, tensor_scale, rows, cols, clip_s, seed, gemm_id,
+                                      rng_stream, out_codes, out_scales, out_tensor_scale, eden_s,
+                                      vbuf, gmax, (hipStream_t)stream);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+size_t fp4nv_ctx_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
+  return nv_operand_bytes(m, k) + nv_operand_bytes(n, k);
+}
+
+static int nv_ctx_check(const fp4nv_ctx* ctx) {
+  if (!ctx) return FP4MX_E_NULL;
+  if (!ctx->xq_codes || !ctx->xq_scales || !ctx->xq_tensor_scale || !ctx->wq_codes ||
+      !ctx->wq_scales || !ctx->wq_tensor_scale)
+    return FP4MX_E_NULL;
+  if (!aligned16(ctx->xq_codes) || !aligned16(ctx->wq_codes) || ((uintptr_t)ctx->xq_scales & 1u) ||
+      ((uintptr_t)ctx->wq_scales & 1u) || ((uintptr_t)ctx->xq_tensor_scale & 3u) ||
+      ((uintptr_t)ctx->wq_tensor_scale & 3u))
+    return FP4MX_E_ALIGN;
+  return FP4MX_OK;
+}
+
+size_t fp4nv_linear_fwd_ctx_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
+  return 512 + fp4nv_gemm_workspace_bytes(m, n, k);
+}
+
+int fp4nv_linear_fwd_ctx(const void* x, const void* w, int64_t m, int64_t n, int64_t k, float* y,
+                         const fp4nv_ctx* ctx, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !w || !y) return FP4MX_E_NULL;
+  int st = nv_ctx_check(ctx);
+  if (st) return st;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return FP4MX_E_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4nv_linear_fwd_ctx_workspace_bytes(m, n, k)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Carver cv{static_cast<uint8_t*>(ws)};
+  uint32_t* amax_x = reinterpret_cast<uint32_t*>(cv.take(4));
+  uint32_t* amax_w = reinterpret_cast<uint32_t*>(cv.take(4));
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* wb = static_cast<const uint16_t*>(w);
+  hipError_t e = launch_nv_amax(xb, m, k, k, amax_x, s);
+  if (e == hipSuccess) e = launch_nv_amax(wb, n, k, k, amax_w, s);
+  if (e == hipSuccess)
+    e = launch_nv_quant(xb, m, k, k, 1, amax_x, ctx->xq_codes, ctx->xq_scales, ctx->xq_tensor_scale, s);
+  if (e == hipSuccess)
+    e = launch_nv_quant(wb, n, k, k, 1, amax_w, ctx->wq_codes, ctx->wq_scales, ctx->wq_tensor_scale, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return nv_gemm_impl(ctx->xq_codes, ctx->xq_scales, ctx->xq_tensor_scale, ctx->wq_codes,
+                      ctx->wq_scales, ctx->wq_tensor_scale, m, n, k, y, n, cv.p, s);
+}
+
+int fp4nv_linear_bwd_ctx(const void* dy, const fp4nv_ctx* ctx, int64_t m, int64_t n, int64_t k,
+                         float* dx, float* dw, void* ws, size_t ws_bytes, void* stream) {
+  if (!dy || !dx || !dw) return FP4MX_E_NULL;
+  int st = nv_ctx_check(ctx);
+  if (st) return st;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k) || m % 128 != 0 || n % 128 != 0) return FP4MX_E_SHAPE;
+  if (!aligned16(dy) || !aligned16(dx) || !aligned16(dw)) return FP4MX_E_ALIGN;
+  if (!ws || ws_bytes < fp4nv_linear_bwd_workspace_bytes(m, n, k)) return FP4MX_E_WORKSPACE;
+  if (!aligned16(ws)) return FP4MX_E_ALIGN;
+  if ((st = check_device())) return st;
+  const NvSrc xs{nullptr, ctx->xq_codes, ctx->xq_scales, ctx->xq_tensor_scale};
+  const NvSrc wsrc{nullptr, ctx->wq_codes, ctx->wq_scales, ctx->wq_tensor_scale};
+  return nv_bwd_impl(dy, xs, wsrc, m, n, k, ctx->seed, dx, dw, static_cast<uint8_t*>(ws),
+                     (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -82,6 +82,12 @@ hipError_t launch_msedn(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
                         float clip_s, uint64_t seed, uint32_t gemm_id, uint32_t stream,
                         uint8_t* codes, uint8_t* scales, float* tensor_scale, float* eden_s,
                         float* vbuf, uint32_t* gmax, hipStream_t s);
+// MS-EDEN of the transpose of a saved NVFP4 operand [rows][cols] (rows % 128 == 0).
+hipError_t launch_msedn_requant(const uint8_t* qcodes, const uint8_t* qscales, const float* qg,
+                                int64_t rows, int64_t cols, float clip_s, uint64_t seed,
+                                uint32_t gemm_id, uint32_t stream, uint8_t* codes, uint8_t* scales,
+                                float* tensor_scale, float* eden_s, float* vbuf, uint32_t* gmax,
+                                hipStream_t s);
 void msedn_sign_words(uint64_t seed, uint32_t gemm_id, uint32_t (&w)[4]);
 
 hipError_t launch_nv_sr(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,

@@ -274,6 +274,73 @@ __global__ __launch_bounds__(256) void msedn_pass1_col(
 }
 
 // ---------------------------------------------------------------------------
+// Pass 1 on a saved NVFP4 operand (the backward's re-quantization of the
+// forward's Q(X), Q(W)): a 128 x 64 tile of codes and E4M3 scales is decoded
+// to fp32 values fl(fl(q * s16) * g) in LDS (q * s16 is exact), then each quad
+// takes one column's 128-chunk as above.  Output row = input column.
+// ---------------------------------------------------------------------------
+constexpr int kFPitch = 65;  // floats per LDS row: 2-way conflicts between quads at most
+
+// OCP E4M3FN byte -> float (exact); 0x7F / 0xFF are NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  if ((b & 0x7Fu) == 0x7Fu) v = __builtin_nanf("");
+  return (b & 0x80u) ? -v : v;
+}
+
+__global__ __launch_bounds__(256) void msedn_pass1_col_nv(
+    const uint8_t* __restrict__ qcodes, const uint8_t* __restrict__ qscales,
+    const float* __restrict__ qg, int64_t rows, int64_t cols, Mask128 mask, float clip_s,
+    uint8_t* __restrict__ codes, float* __restrict__ vbuf, float* __restrict__ eden_s,
+    uint32_t* __restrict__ gmax) {
+  __shared__ float tile[128 * kFPitch];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 128, cb = (int64_t)blockIdx.y * 64;
+  const int nc = (int)min<int64_t>(64, cols - cb);
+  {
+    // thread = 32 consecutive elements of one source row: row tid/2, half tid&1
+    const int r = tid >> 1, h = tid & 1;
+    if (h * 32 < nc) {
+      const int64_t row = r0 + r, c0 = cb + 32 * h;
+      const float g = *qg;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qcodes + row * (cols / 2) + c0 / 2);
+      const uint32_t sw = *reinterpret_cast<const uint16_t*>(qscales + row * (cols / 16) + c0 / 16);
+      const float s0 = e4m3_to_f32(sw & 0xFFu), s1 = e4m3_to_f32(sw >> 8);
+      const uint32_t cw[4] = {v.x, v.y, v.z, v.w};
+      float* d = tile + r * kFPitch + 32 * h;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t q = (cw[i / 8] >> (4 * (i % 8))) & 0xFu;
+        const float qv = __uint_as_float(__float_as_uint(e2m1_mag(q & 7u)) | ((q & 8u) << 28));
+        d[i] = (qv * (i < 16 ? s0 : s1)) * g;
+      }
+    }
+  }
+  __syncthreads();
+  const int c = tid >> 2, l4 = tid & 3;
+  const bool live = c < nc;
+  const int cc = live ? c : 0;
+  float tv[32];
+  const uint32_t m = mask.w[l4];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float x = tile[(32 * l4 + i) * kFPitch + cc];
+    tv[i] = __uint_as_float(__float_as_uint(x) ^ (((m >> i) & 1u) << 31));
+  }
+  uint32_t cw[4];
+  float v[2], S;
+  msedn_core(tv, l4, clip_s, cw, v, S);
+  if (live) {
+    const int64_t orow = cb + c, ocol = r0 + 32 * l4;
+    *reinterpret_cast<u32x4*>(codes + orow * (rows / 2) + ocol / 2) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+    *reinterpret_cast<float2*>(vbuf + orow * (rows / 16) + ocol / 16) = make_float2(v[0], v[1]);
+    if (eden_s && l4 == 0) eden_s[orow * (rows / 128) + r0 / 128] = S;
+  }
+  block_max_atomic(live ? fmaxf(v[0], v[1]) : 0.0f, gmax);
+}
+
+// ---------------------------------------------------------------------------
 // Pass 2: thread = one group scale.  k = least integer with max * 2^-k <= 256;
 // scale = SR_E4M3(v * 2^-k) with u = (r >> 8) * 2^-24, r = hash of the
 // scale's flat index in the output operand.
@@ -318,6 +385,24 @@ __global__ __launch_bounds__(256) void msedn_pass2(const float* __restrict__ vbu
 }
 
 }  // namespace
+
+hipError_t launch_msedn_requant(const uint8_t* qcodes, const uint8_t* qscales, const float* qg,
+                                int64_t rows, int64_t cols, float clip_s, uint64_t seed,
+                                uint32_t gemm_id, uint32_t stream, uint8_t* codes, uint8_t* scales,
+                                float* tensor_scale, float* eden_s, float* vbuf, uint32_t* gmax,
+                                hipStream_t s) {
+  Mask128 m;
+  msedn_sign_words(seed, gemm_id, m.w);
+  const RngKey key = make_key(seed, stream);
+  hipLaunchKernelGGL(msedn_zero, dim3(1), dim3(1), 0, s, gmax);
+  hipLaunchKernelGGL(msedn_pass1_col_nv, dim3((unsigned)(rows / 128), (unsigned)((cols + 63) / 64)),
+                     dim3(256), 0, s, qcodes, qscales, qg, rows, cols, m, clip_s, codes, vbuf,
+                     eden_s, gmax);
+  const int64_t nscales = cols * (rows / 16);
+  hipLaunchKernelGGL(msedn_pass2, dim3((unsigned)((nscales + 255) / 256)), dim3(256), 0, s, vbuf,
+                     gmax, (uint64_t)nscales, key.lo, key.hi, scales, tensor_scale);
+  return hipGetLastError();
+}
 
 void msedn_sign_words(uint64_t seed, uint32_t gemm_id, uint32_t (&w)[4]) {
   const uint64_t a = splitmix64(seed ^ ((uint64_t)(0x5200u + 2u * gemm_id) << 32));

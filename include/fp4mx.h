@@ -362,6 +362,55 @@ FP4MX_API int fp4nv_linear_bwd(const void* dy, const void* x, const void* w, int
                      int64_t k, uint64_t seed, float* dx, float* dw, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* ------------------------------------------------------------------------
+ * Re-quantization of the saved forward operands for the NVFP4 backward
+ * (source: "Quartet II ..." -- "The Complete Quartet II Computation Graph":
+ * de-quantize the saved Q(X), Q(W), transpose, RHT on the inner dimension with
+ * a seed shared by both operands of a GEMM, MS-EDEN, NVFP4 GEMM, no inverse
+ * RHT; "Forward Pass Design: The Representation-Requantization Trade-Off").
+ * ------------------------------------------------------------------------ */
+
+/* MS-EDEN of the transpose of a saved NVFP4 operand A [rows][cols] (codes
+ * [rows][cols/2], E4M3 scales [rows][cols/16], device fp32 tensor scale): the
+ * values fl32(q * s16 * g) (one rounding of the exact product) are transposed
+ * and quantized as fp4nv_msedn_quantize does along rows of the transpose
+ * (128-chunks along the original rows; rows % 128 == 0): out_codes
+ * [cols][rows/2], out_scales [cols][rows/16], out_tensor_scale, optional
+ * eden_s [cols][rows/128].  ws: fp4nv_msedn_workspace_bytes(rows, cols). */
+FP4MX_API int fp4nv_msedn_requantize(const uint8_t* codes, const uint8_t* scales,
+                           const float* tensor_scale, int64_t rows, int64_t cols, float clip_s,
+                           uint64_t seed, uint32_t gemm_id, uint32_t rng_stream,
+                           uint8_t* out_codes, uint8_t* out_scales, float* out_tensor_scale,
+                           float* eden_s, void* ws, size_t ws_bytes, void* stream);
+
+/* Saved forward operands of the NVFP4 layer: Q(X) [m][k] and Q(W) [n][k]
+ * (codes, E4M3 scales, device fp32 tensor scale each), and the backward seed.
+ * Caller-owned device memory; fp4nv_ctx_bytes bounds the six buffers. */
+typedef struct {
+  uint8_t* xq_codes;
+  uint8_t* xq_scales;
+  float* xq_tensor_scale;
+  uint8_t* wq_codes;
+  uint8_t* wq_scales;
+  float* wq_tensor_scale;
+  uint64_t seed;
+} fp4nv_ctx;
+
+FP4MX_API size_t fp4nv_ctx_bytes(int64_t m, int64_t n, int64_t k);
+FP4MX_API size_t fp4nv_linear_fwd_ctx_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* Forward as fp4nv_linear_fwd (RTN + 4/6, FP8-staged GEMM), with Q(X) and
+ * Q(W) written into ctx for the backward. */
+FP4MX_API int fp4nv_linear_fwd_ctx(const void* x, const void* w, int64_t m, int64_t n, int64_t k,
+                         float* y, const fp4nv_ctx* ctx, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward from the saved operands: dX = gemm(MSEDEN(dY), MSEDEN(deq(Q(W))^T))
+ * (inner n; GEMM id 1, streams 5 and 6), dW = gemm(MSEDEN(dY^T),
+ * MSEDEN(deq(Q(X))^T)) (inner m; GEMM id 2, streams 7 and 8), seed ctx->seed,
+ * clip 6.  m % 128 == n % 128 == 0; ws: fp4nv_linear_bwd_workspace_bytes. */
+FP4MX_API int fp4nv_linear_bwd_ctx(const void* dy, const fp4nv_ctx* ctx, int64_t m, int64_t n,
+                         int64_t k, float* dx, float* dw, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

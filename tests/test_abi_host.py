@@ -129,3 +129,19 @@ def test_quest_validation():
     m, n, k = 8192, 4096, 4096
     assert L.fp4mx_quest_ctx_bytes(m, n, k) == (m * k + n * k) * 17 // 32 + (m * k + n * k) // 8
     assert L.fp4mx_quest_bwd_workspace_bytes(m, n, k) == (2 * m * n + k * n + k * m) * 17 // 32
+
+
+def test_nv_requant_and_ctx_validation():
+    L = binding.lib()
+    keep, p = _buf()
+    f = C.c_void_p(p.value)
+    assert L.fp4nv_msedn_requantize(p, p, f, 96, 64, 6.0, 0, 1, 6, p, p, f, None, p, 1 << 20, None) == -2
+    assert L.fp4nv_msedn_requantize(p, p, f, 128, 64, 0.0, 0, 1, 6, p, p, f, None, p, 1 << 20, None) == -4
+    assert L.fp4nv_msedn_requantize(p, p, None, 128, 64, 6.0, 0, 1, 6, p, p, f, None, p, 1 << 20, None) == -1
+    assert L.fp4nv_msedn_requantize(p, p, f, 128, 64, 6.0, 0, 1, 6, p, p, f, None, p, 16, None) == -5
+    ctx = binding.NvCtxStruct(p.value, p.value, p.value, p.value, p.value, p.value, 0)
+    assert L.fp4nv_linear_fwd_ctx(p, p, 64, 64, 64, f, C.byref(ctx), p, 16, None) == -5
+    assert L.fp4nv_linear_bwd_ctx(p, C.byref(ctx), 128, 96, 64, f, f, p, 1 << 26, None) == -2
+    bad = binding.NvCtxStruct(p.value, p.value + 1, p.value, p.value, p.value, p.value, 0)
+    assert L.fp4nv_linear_bwd_ctx(p, C.byref(bad), 128, 128, 64, f, f, p, 1 << 26, None) == -3
+    assert L.fp4nv_linear_bwd_ctx(p, None, 128, 128, 64, f, f, p, 1 << 26, None) == -1
