@@ -442,6 +442,56 @@ def time_nvfp4_bwd(steps, warmup):
     return res
 
 
+def time_quartet2(steps, warmup):
+    """The Quartet II graph on the Quartet layer: NVFP4 forward keeping Q(X),
+    Q(W) and the backward re-quantizing them with MS-EDEN (6MNK flop per
+    step), plus the re-quantizer alone on the saved Q(X) (8192 x 4096) against
+    its algorithmic bytes (0.5 + 1/16 B read, 0.5 + 1/16 B written per element)."""
+    import torch
+    import fp4_microscaled_quantized_amd as fq
+    from fp4_microscaled_quantized_amd import synth
+    from fp4_microscaled_quantized_amd.binding import _ptr, _stream
+    d = synth.quartet_linear(0)
+    x, w, dy = dev_bf16(d["x"]), dev_bf16(d["w"]), dev_bf16(d["dy"])
+    m, k = x.shape
+    n = w.shape[0]
+    L = fq.lib()
+    wsf = torch.empty(L.fp4nv_linear_fwd_ctx_workspace_bytes(m, n, k), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(L.fp4nv_linear_bwd_workspace_bytes(m, n, k), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    dx = torch.empty((m, k), dtype=torch.float32, device="cuda")
+    dw = torch.empty((n, k), dtype=torch.float32, device="cuda")
+    _, ctx = fq.nv_linear_fwd_ctx(x, w, seed=0, ws=wsf, out=y)
+
+    def step(i):
+        fq.nv_linear_fwd_ctx(x, w, seed=i, ws=wsf, out=y)
+        ctx.seed = i
+        fq.nv_linear_bwd_ctx(dy, ctx, ws=wsb, dx=dx, dw=dw)
+    ms = _time_calls(step, steps, warmup)
+    fwd_ms = _time_calls(lambda i: fq.nv_linear_fwd_ctx(x, w, seed=i, ws=wsf, out=y), steps, warmup)
+    res = {"workload": "Quartet II graph: NVFP4 RTN+4/6 fwd (saved Q(X), Q(W)) + MS-EDEN bwd "
+                       "re-quantizing them, M=8192 N=K=4096",
+           "ms_per_step": round(ms, 4), "TFLOP/s": round(6.0 * m * n * k / (ms * 1e-3) / 1e12, 1),
+           "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(ms - fwd_ms, 4)}
+    del wsb
+    out_c = torch.empty((k, m // 2), dtype=torch.uint8, device="cuda")
+    out_s = torch.empty((k, m // 16), dtype=torch.uint8, device="cuda")
+    out_g = torch.empty(1, dtype=torch.float32, device="cuda")
+    qws = torch.empty(L.fp4nv_msedn_workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    st = _stream(x.device)
+    xq = ctx.xq
+    call = lambda i: L.fp4nv_msedn_requantize(_ptr(xq.codes), _ptr(xq.scales), _ptr(xq.tensor_scale), m, k,
+                                              6.0, i, 2, 8, _ptr(out_c), _ptr(out_s), _ptr(out_g), None,
+                                              _ptr(qws), qws.numel(), st)
+    assert call(0) == 0
+    qms = _time_calls(call, max(steps, 20), warmup)
+    alg = m * k * 2 * (0.5 + 1 / 16)
+    res["requant_q_x"] = {"us": round(qms * 1e3, 2), "GB/s": round(alg / (qms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(alg / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "algorithmic_bytes": int(alg)}
+    return res
+
+
 def cpu_baseline(rows=256):
     """The oracle's linear fwd+bwd on the first `rows` tokens of the headline workload."""
     from fp4_microscaled_quantized_amd import synth
@@ -526,6 +576,8 @@ def main():
         out["nvfp4_bwd_ms_eden"] = time_nvfp4_bwd(max(a.steps // 2, 5), 2)
         torch.cuda.empty_cache()
         out["quest_linear"] = time_quest(a.steps, a.warmup)
+        torch.cuda.empty_cache()
+        out["nvfp4_quartet2"] = time_quartet2(max(a.steps // 2, 5), 2)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
