@@ -101,6 +101,11 @@ __device__ __forceinline__ void quant_group(const float (&y)[kGroup], uint32_t i
   } else {
     // f = 0.75 * 2^(127-code), exactly representable for code <= 254.
     const float f = __builtin_ldexpf(0.75f, 127 - code);
+    // The group's first index is a multiple of 32, so element i hashes
+    // idx_lo ^ i, and the first xor-shift of fmix32 touches only the group
+    // part: h1 ^ i equals that step's result for element i.
+    const uint32_t h0 = idx_lo ^ kmix;
+    const uint32_t h1 = h0 ^ (h0 >> 16);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t word = 0;
@@ -108,19 +113,20 @@ __device__ __forceinline__ void quant_group(const float (&y)[kGroup], uint32_t i
       for (int j = 0; j < 8; ++j) {
         const int i = 8 * k + j;
         const float v = __builtin_fabsf(y[i]) * f;  // 0 <= v < 6
-        const uint32_t vb = __float_as_uint(v);
-        const uint32_t r = fmix32((idx_lo + (uint32_t)i) ^ kmix);
-        // round up iff (r >> 8) * 2^-24 < (v - a) / (b - a):
-        //  v in [1, 6):   (v-a)/(b-a) = frac22 / 2^22  ->  (r >> 10) < frac22
-        //  v in [0.5, 1): (v-a)/(b-a) = frac23 / 2^23  ->  (r >> 9)  < frac23
-        //  v < 0.5:       (v-a)/(b-a) = 2v             ->  (r >> 8) < v * 2^25
-        const bool hi = vb >= 0x3F800000u;
-        const uint32_t lim = vb & (hi ? 0x3FFFFFu : 0x7FFFFFu);
-        const uint32_t rr = r >> (hi ? 10 : 9);
-        const uint32_t base = hi ? (vb >> 22) - 252u : 1u;
-        const uint32_t qa = base + (rr < lim ? 1u : 0u);
-        const uint32_t qb = (float)(r >> 8) < v * 0x1p25f ? 1u : 0u;
-        uint32_t q = vb >= 0x3F000000u ? qa : qb;
+        uint32_t r = (h1 ^ (uint32_t)i) * 0x85EBCA6Bu;
+        r ^= r >> 13;
+        r *= 0xC2B2AE35u;
+        r ^= r >> 16;
+        // Grid position: with e = max(floor(log2 v), 0), w = v 2^(1-e) lies in
+        // [0, 4) and element code floor(w) + 2e is the grid point below v;
+        // the gap to the next one maps to [0, 1) as frac(w) exactly (powers
+        // of two only).  Up iff (r >> 8) 2^-24 < frac(w), i.e. the
+        // probability (v - a) / (b - a) with a 24-bit uniform.
+        const uint32_t eb = max(__float_as_uint(v) >> 23, 127u);  // 127 + e
+        const float w = __builtin_ldexpf(v, 128 - (int)eb);
+        const float fr = __builtin_amdgcn_fractf(w);  // w - floor(w), exact for w >= 0
+        const uint32_t up = (float)(r >> 8) < fr * 0x1p24f ? 1u : 0u;
+        uint32_t q = (uint32_t)w + 2u * (eb - 127u) + up;  // truncation = floor for w >= 0
         q |= (__float_as_uint(y[i]) >> 28) & 8u;
         word |= q << (4 * j);
       }
