@@ -341,20 +341,17 @@ def time_quantizer(steps, warmup, nbuf=6):
         def call(i):
             _check(L.fp4mx_hadamard_quantize(_ptr(xs[i % nbuf]), R, Cc, Cc, fq.ROW, rnd, mask, 0, 1,
                                              _ptr(outs[i % nbuf][0]), _ptr(outs[i % nbuf][1]), _stream()))
-        for i in range(warmup):
-            call(i)
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        ev[0].record()
-        for i in range(steps):
-            call(i)
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+        # back-to-back launches, events only around the whole run
+        ms = _time_calls(call, steps, warmup)
         byt = R * Cc * MX_BYTES_PER_ELEM
         gbs = byt / (ms * 1e-3) / 1e9
         res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                      "bytes_per_launch": int(byt)}
+    # context: a plain device copy of the same bf16 tensor (read + write 2 B per
+    # element) over the same rotating buffers, i.e. what streaming reaches at this size
+    ys = [torch.empty_like(x0) for _ in range(nbuf)]
+    cms = _time_calls(lambda i: ys[i % nbuf].copy_(xs[i % nbuf]), steps, warmup)
+    res["copy_bf16_GB/s"] = round(R * Cc * 4 / (cms * 1e-3) / 1e9, 1)
     return {"workload": "quantizer 8192x4096 bf16, half N(0,1) half Student-t(3), RHT-32, row axis",
             "rotating_buffers_MB": round(nbuf * (R * Cc * 2 + R * Cc * 17 // 32) / 1e6, 1), **res}
 
