@@ -337,10 +337,15 @@ def time_quantizer(steps, warmup, nbuf=6):
     L = fq.lib()
     mask = fq.sign_mask(0, 0)
     res = {}
-    for name, rnd in (("rtn", fq.RTN), ("sr", fq.SR)):
-        def call(i):
-            _check(L.fp4mx_hadamard_quantize(_ptr(xs[i % nbuf]), R, Cc, Cc, fq.ROW, rnd, mask, 0, 1,
-                                             _ptr(outs[i % nbuf][0]), _ptr(outs[i % nbuf][1]), _stream()))
+    outs_t = [(torch.empty((Cc, R // 2), dtype=torch.uint8, device="cuda"),
+               torch.empty((Cc, R // 32), dtype=torch.uint8, device="cuda")) for _ in range(nbuf)]
+    for name, rnd, axis in (("rtn", fq.RTN, fq.ROW), ("sr", fq.SR, fq.ROW),
+                            ("rtn_col", fq.RTN, fq.COL), ("sr_col", fq.SR, fq.COL)):
+        o = outs if axis == fq.ROW else outs_t
+
+        def call(i, rnd=rnd, axis=axis, o=o):
+            _check(L.fp4mx_hadamard_quantize(_ptr(xs[i % nbuf]), R, Cc, Cc, axis, rnd, mask, 0, 1,
+                                             _ptr(o[i % nbuf][0]), _ptr(o[i % nbuf][1]), _stream()))
         # back-to-back launches, events only around the whole run
         ms = _time_calls(call, steps, warmup)
         byt = R * Cc * MX_BYTES_PER_ELEM
@@ -352,7 +357,8 @@ def time_quantizer(steps, warmup, nbuf=6):
     ys = [torch.empty_like(x0) for _ in range(nbuf)]
     cms = _time_calls(lambda i: ys[i % nbuf].copy_(xs[i % nbuf]), steps, warmup)
     res["copy_bf16_GB/s"] = round(R * Cc * 4 / (cms * 1e-3) / 1e9, 1)
-    return {"workload": "quantizer 8192x4096 bf16, half N(0,1) half Student-t(3), RHT-32, row axis",
+    return {"workload": "quantizer 8192x4096 bf16, half N(0,1) half Student-t(3), RHT-32; row axis "
+                        "(rtn, sr) and column axis, i.e. the transposed operand (rtn_col, sr_col)",
             "rotating_buffers_MB": round(nbuf * (R * Cc * 2 + R * Cc * 17 // 32) / 1e6, 1), **res}
 
 
@@ -377,8 +383,25 @@ def time_nvfp4(steps, warmup):
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / steps
     tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    # the quantizer (tensor amax pass + RTN/4-over-6 pass) on X alone
+    from fp4_microscaled_quantized_amd.binding import _ptr, _stream
+    L = fq.lib()
+    qc = torch.empty((m, k // 2), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((m, k // 16), dtype=torch.uint8, device="cuda")
+    qg = torch.empty(1, dtype=torch.float32, device="cuda")
+    qws = torch.empty(L.fp4nv_quantize_workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    qcall = lambda i: L.fp4nv_quantize46(_ptr(x), m, k, k, 1, _ptr(qc), _ptr(qs), _ptr(qg), _ptr(qws),
+                                         qws.numel(), _stream())
+    assert qcall(0) == 0
+    qms = _time_calls(qcall, max(steps, 10), 2)
+    two = m * k * (2 + 2 + 0.5 + 1 / 16)
+    one = m * k * (2 + 0.5 + 1 / 16)
     return {"workload": "NVFP4 RTN+4/6 linear fwd 16384x8192->8192", "ms": round(ms, 4),
-            "TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+            "TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "quantizer_x_16384x8192": {"us": round(qms * 1e3, 1),
+                                       "GB/s_two_pass_bytes": round(two / (qms * 1e-3) / 1e9, 1),
+                                       "frac_hbm_two_pass": round(two / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                       "GB/s_one_read_bytes": round(one / (qms * 1e-3) / 1e9, 1)}}
 
 
 def _time_calls(call, steps, warmup):
