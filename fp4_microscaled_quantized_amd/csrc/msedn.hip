@@ -53,10 +53,30 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, 0.0f, 1.0f, 0) & 0xFu;
 }
 
-__device__ __forceinline__ float e2m1_mag(uint32_t q) {  // 0, .5, 1, 1.5, 2, 3, 4, 6
-  const uint32_t e = q >> 1, m = q & 1u;
-  return e == 0 ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
+// Value of lane l ^ 1 (CTRL 0xB1, quad_perm [1,0,3,2]) or l ^ 2 (CTRL 0x4E,
+// quad_perm [2,3,0,1]) within each quad of lanes, by DPP (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float quad_xor(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, 0xF, 0xF, false));
 }
+__device__ __forceinline__ float quad_xor1(float v) { return quad_xor<0xB1>(v); }
+__device__ __forceinline__ float quad_xor2(float v) { return quad_xor<0x4E>(v); }
+
+// Two E2M1 codes (byte B of w) -> their signed values, exact (gfx950's
+// converter with scale 1.0); and the codes of two values into byte B.
+template <int B>
+__device__ __forceinline__ void e2m1_pair(uint32_t w, float& lo, float& hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+  lo = v.x;
+  hi = v.y;
+}
+template <int B>
+__device__ __forceinline__ uint32_t e2m1_pack(uint32_t w, float v0, float v1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v0, v1, 1.0f, B);
+}
+
 
 // fp32 rounded to 4 significant bits (nearest, ties to even) on its encoding.
 __device__ __forceinline__ float e8m3_rne(float x) {
@@ -91,13 +111,19 @@ __device__ __forceinline__ void msedn_core(float (&t)[32], int l4, float clip_s,
   }
   // stages h = 32 (lane l4 ^ 1) and h = 64 (lane l4 ^ 2): the lower lane keeps
   // a + b, the upper lane a - b with a from the lower lane
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const int bit = 1 << st;
-    const bool upper = (l4 & bit) != 0;
+  {
+    const bool upper = (l4 & 1) != 0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const float o = __shfl_xor(t[i], bit, 64);
+      const float o = quad_xor1(t[i]);
+      t[i] = upper ? o - t[i] : t[i] + o;
+    }
+  }
+  {
+    const bool upper = (l4 & 2) != 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float o = quad_xor2(t[i]);
       t[i] = upper ? o - t[i] : t[i] + o;
     }
   }
@@ -116,8 +142,8 @@ __device__ __forceinline__ void msedn_core(float (&t)[32], int l4, float clip_s,
   // chunk exponent E: 2^E <= max|y| < 2^(E+1) (0 for a zero chunk); the dot
   // products use y * 2^-E so no square overflows
   float cm = fmaxf(am2[0], am2[1]);
-  cm = fmaxf(cm, __shfl_xor(cm, 1, 64));
-  cm = fmaxf(cm, __shfl_xor(cm, 2, 64));
+  cm = fmaxf(cm, quad_xor1(cm));
+  cm = fmaxf(cm, quad_xor2(cm));
   const uint32_t cb = __float_as_uint(cm);
   const int E = cb == 0 ? 0 : (cb >= 0x800000u ? (int)(cb >> 23) - 127 : (31 - __builtin_clz(cb)) - 149);
 #pragma unroll
@@ -125,43 +151,65 @@ __device__ __forceinline__ void msedn_core(float (&t)[32], int l4, float clip_s,
     const float p = e8m3_rne(am2[gi] / clip_s);  // IEEE division
     v[gi] = p;
     // q = E2M1_RNE(fl(y / p)): fl(y * fl(1/p)) is within 3 ulp of fl(y / p),
-    // so equal codes at v (1 -+ 2^-21) settle it; otherwise divide exactly
-    uint32_t q[16];
+    // so equal codes at v (1 -+ 2^-21) settle it (compared eight codes per
+    // word); otherwise divide exactly
     const float rcp = p > 0.0f ? 1.0f / p : 0.0f;
     bool exact = !(p > 0.0f) || !(rcp < __builtin_inff());
+    uint32_t cw[2] = {0u, 0u};
     if (!exact) {
+      constexpr float kLo = 1.0f - 0x1p-21f, kHi = 1.0f + 0x1p-21f;
+      uint32_t hw[2] = {0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float w = t[16 * gi + i] * rcp;
-        const uint32_t pr = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-            0u, w * (1.0f - 0x1p-21f), w * (1.0f + 0x1p-21f), 1.0f, 0);
-        q[i] = pr & 0xFu;
-        exact |= (pr & 0xFu) != ((pr >> 4) & 0xFu);
+      for (int w = 0; w < 2; ++w) {
+        float u[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[i] = t[16 * gi + 8 * w + i] * rcp;
+        cw[w] = e2m1_pack<0>(cw[w], u[0] * kLo, u[1] * kLo);
+        hw[w] = e2m1_pack<0>(hw[w], u[0] * kHi, u[1] * kHi);
+        cw[w] = e2m1_pack<1>(cw[w], u[2] * kLo, u[3] * kLo);
+        hw[w] = e2m1_pack<1>(hw[w], u[2] * kHi, u[3] * kHi);
+        cw[w] = e2m1_pack<2>(cw[w], u[4] * kLo, u[5] * kLo);
+        hw[w] = e2m1_pack<2>(hw[w], u[4] * kHi, u[5] * kHi);
+        cw[w] = e2m1_pack<3>(cw[w], u[6] * kLo, u[7] * kLo);
+        hw[w] = e2m1_pack<3>(hw[w], u[6] * kHi, u[7] * kHi);
       }
+      exact = (cw[0] != hw[0]) || (cw[1] != hw[1]);
     }
     if (exact) {
+      cw[0] = cw[1] = 0u;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        q[i] = p > 0.0f ? e2m1_code(t[16 * gi + i] / p) : (__float_as_uint(t[16 * gi + i]) >> 28) & 8u;
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t q =
+            p > 0.0f ? e2m1_code(t[16 * gi + i] / p) : (__float_as_uint(t[16 * gi + i]) >> 28) & 8u;
+        cw[i / 8] |= q << (4 * (i % 8));
+      }
     }
-    codes[2 * gi] = codes[2 * gi + 1] = 0;
+    codes[2 * gi] = cw[0];
+    codes[2 * gi + 1] = cw[1];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      codes[2 * gi + i / 8] |= q[i] << (4 * (i % 8));
-      const float y = t[16 * gi + i];
-      const float r = __uint_as_float(__float_as_uint(e2m1_mag(q[i] & 7u)) | ((q[i] & 8u) << 28)) * p;
-      const float z = __builtin_ldexpf(y, -E), zr = __builtin_ldexpf(r, -E);
-      num[16 * gi + i] = z * z;
-      den[16 * gi + i] = z * zr;
+    for (int w = 0; w < 2; ++w) {
+      float qv[8];
+      e2m1_pair<0>(cw[w], qv[0], qv[1]);
+      e2m1_pair<1>(cw[w], qv[2], qv[3]);
+      e2m1_pair<2>(cw[w], qv[4], qv[5]);
+      e2m1_pair<3>(cw[w], qv[6], qv[7]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = 16 * gi + 8 * w + i;
+        const float r = qv[i] * p;
+        const float z = __builtin_ldexpf(t[k], -E), zr = __builtin_ldexpf(r, -E);
+        num[k] = z * z;
+        den[k] = z * zr;
+      }
     }
   }
   float sn = tree32(num), sd = tree32(den);
   // quad tree: (l0 + l1) + (l2 + l3); fp32 addition commutes, so every lane
   // ends with the same value
-  sn = sn + __shfl_xor(sn, 1, 64);
-  sd = sd + __shfl_xor(sd, 1, 64);
-  sn = sn + __shfl_xor(sn, 2, 64);
-  sd = sd + __shfl_xor(sd, 2, 64);
+  sn = sn + quad_xor1(sn);
+  sd = sd + quad_xor1(sd);
+  sn = sn + quad_xor2(sn);
+  sd = sd + quad_xor2(sd);
   S = sd > 0.0f ? sn / sd : 1.0f;  // IEEE division
   v[0] = S * v[0];
   v[1] = S * v[1];
@@ -209,7 +257,7 @@ __global__ __launch_bounds__(256) void msedn_pass1_row(
   uint32_t wd[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const u32x4 v = __builtin_nontemporal_load(src + q);
+    const u32x4 v = *(src + q);
     wd[4 * q] = v.x; wd[4 * q + 1] = v.y; wd[4 * q + 2] = v.z; wd[4 * q + 3] = v.w;
   }
   float tv[32];
@@ -310,10 +358,14 @@ __global__ __launch_bounds__(256) void msedn_pass1_col_nv(
       const uint32_t cw[4] = {v.x, v.y, v.z, v.w};
       float* d = tile + r * kFPitch + 32 * h;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const uint32_t q = (cw[i / 8] >> (4 * (i % 8))) & 0xFu;
-        const float qv = __uint_as_float(__float_as_uint(e2m1_mag(q & 7u)) | ((q & 8u) << 28));
-        d[i] = (qv * (i < 16 ? s0 : s1)) * g;
+      for (int w = 0; w < 4; ++w) {
+        float qv[8];
+        e2m1_pair<0>(cw[w], qv[0], qv[1]);
+        e2m1_pair<1>(cw[w], qv[2], qv[3]);
+        e2m1_pair<2>(cw[w], qv[4], qv[5]);
+        e2m1_pair<3>(cw[w], qv[6], qv[7]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[8 * w + i] = (qv[i] * (w < 2 ? s0 : s1)) * g;
       }
     }
   }
