@@ -42,8 +42,8 @@ MX_BYTES_PER_ELEM = 2 + 0.5 + 1 / 32   # bf16 in, 4-bit code + 1/32 scale byte o
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", choices=["quartet", "llama"], default="quartet")
     p.add_argument("--no-extra", action="store_true", help="only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -62,17 +62,18 @@ class _Step:
 
     def run(self, steps, timed):
         """`steps` passes of the launches, back to back; when timed, one event
-        per step boundary (no events between the kernels of a step)."""
+        before the first and one after the last launch (nothing is inserted
+        between steps or kernels)."""
         import torch
         calls = self._calls()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)] if timed else None
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)] if timed else None
         if timed:
             evs[0].record()
-        for i in range(steps):
+        for _ in range(steps):
             for c in calls:
                 c()
-            if timed:
-                evs[i + 1].record()
+        if timed:
+            evs[1].record()
         return evs
 
     def kernel_times(self, steps):
@@ -242,7 +243,7 @@ def time_step(st, steps, warmup):
     evs = st.run(steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    step_ms = [evs[0].elapsed_time(evs[1]) / steps]
     st.kernel_times(steps)
     avg = {nm: float(np.mean(v)) for nm, v in st.times.items()}
     return wall, avg, step_ms
