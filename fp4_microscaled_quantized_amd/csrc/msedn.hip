@@ -239,38 +239,60 @@ __device__ __forceinline__ void unpack_signed(const uint32_t (&wd)[16], uint32_t
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1, row axis: thread = 32 elements; quad = one 128-chunk of one row.
+// Pass 1, row axis: thread = 32 elements of each of two chunks; quad g takes
+// chunks 2g and 2g+1 (row-major over (row, chunk-in-row)).  Both chunks' loads
+// are issued before either is transformed, so one memory latency covers two
+// chunks.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void msedn_pass1_row(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, Mask128 mask,
-    float clip_s, uint8_t* __restrict__ codes, float* __restrict__ vbuf,
-    float* __restrict__ eden_s, uint32_t* __restrict__ gmax, FastDiv qdiv, uint32_t nthreads) {
-  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
-  const bool live = t < nthreads;  // every lane takes part in the shuffles
-  const uint32_t tt = live ? t : 0u;
-  const int l4 = (int)(tt & 3u);
-  const uint32_t quad = tt >> 2;                 // chunk index
-  const uint32_t row32 = fastdiv(quad, qdiv);     // qdiv.d = chunks per row
-  const int64_t row = row32, ch = quad - row32 * qdiv.d;
-  const int64_t c0 = ch * 128 + 32 * l4;          // first column of this lane
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ld + c0);
-  uint32_t wd[16];
+__device__ __forceinline__ void load_lane32(const uint16_t* x, int64_t ld, uint32_t chunk, int l4,
+                                            FastDiv qdiv, uint32_t (&wd)[16], int64_t& row,
+                                            int64_t& ch) {
+  const uint32_t row32 = fastdiv(chunk, qdiv);  // qdiv.d = chunks per row
+  row = row32;
+  ch = chunk - row32 * qdiv.d;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ld + ch * 128 + 32 * l4);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const u32x4 v = *(src + q);
     wd[4 * q] = v.x; wd[4 * q + 1] = v.y; wd[4 * q + 2] = v.z; wd[4 * q + 3] = v.w;
   }
-  float tv[32];
-  unpack_signed(wd, mask.w[l4], tv);
-  uint32_t cw[4];
-  float v[2], S;
-  msedn_core(tv, l4, clip_s, cw, v, S);
-  if (live) {
-    *reinterpret_cast<u32x4*>(codes + row * (cols / 2) + c0 / 2) = u32x4{cw[0], cw[1], cw[2], cw[3]};
-    *reinterpret_cast<float2*>(vbuf + row * (cols / 16) + c0 / 16) = make_float2(v[0], v[1]);
-    if (eden_s && l4 == 0) eden_s[row * (cols / 128) + ch] = S;
+}
+
+__global__ __launch_bounds__(256) void msedn_pass1_row(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, Mask128 mask,
+    float clip_s, uint8_t* __restrict__ codes, float* __restrict__ vbuf,
+    float* __restrict__ eden_s, uint32_t* __restrict__ gmax, FastDiv qdiv, uint32_t nthreads,
+    uint32_t nchunks) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  const bool live = t < nthreads;  // every lane takes part in the shuffles
+  const uint32_t tt = live ? t : 0u;
+  const int l4 = (int)(tt & 3u);
+  const uint32_t ca = 2u * (tt >> 2);
+  const bool live_b = live && ca + 1u < nchunks;
+  const uint32_t cb = live_b ? ca + 1u : ca;  // a spare lane re-reads chunk a
+  uint32_t wa[16], wb[16];
+  int64_t row_a, ch_a, row_b, ch_b;
+  load_lane32(x, ld, ca, l4, qdiv, wa, row_a, ch_a);
+  load_lane32(x, ld, cb, l4, qdiv, wb, row_b, ch_b);
+  float vmax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float tv[32];
+    unpack_signed(k == 0 ? wa : wb, mask.w[l4], tv);
+    uint32_t cw[4];
+    float v[2], S;
+    msedn_core(tv, l4, clip_s, cw, v, S);
+    const bool on = k == 0 ? live : live_b;
+    const int64_t row = k == 0 ? row_a : row_b, ch = k == 0 ? ch_a : ch_b;
+    const int64_t c0 = ch * 128 + 32 * l4;
+    if (on) {
+      *reinterpret_cast<u32x4*>(codes + row * (cols / 2) + c0 / 2) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+      *reinterpret_cast<float2*>(vbuf + row * (cols / 16) + c0 / 16) = make_float2(v[0], v[1]);
+      if (eden_s && l4 == 0) eden_s[row * (cols / 128) + ch] = S;
+      vmax = fmaxf(vmax, fmaxf(v[0], v[1]));
+    }
   }
-  block_max_atomic(live ? fmaxf(v[0], v[1]) : 0.0f, gmax);
+  block_max_atomic(vmax, gmax);
 }
 
 // ---------------------------------------------------------------------------
@@ -473,11 +495,12 @@ hipError_t launch_msedn(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
   int64_t nscales;
   if (axis == FP4MX_AXIS_ROW) {
     const int64_t cpr = cols / 128;
-    const uint64_t threads = (uint64_t)rows * (uint64_t)cpr * 4u;
-    if (threads >= (1ull << 31)) return hipErrorInvalidValue;
+    const uint64_t chunks = (uint64_t)rows * (uint64_t)cpr;
+    const uint64_t threads = (chunks + 1) / 2 * 4u;  // a quad per two chunks
+    if (chunks >= (1ull << 31)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(msedn_pass1_row, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                        x, rows, cols, ld, m, clip_s, codes, vbuf, eden_s, gmax,
-                       make_fastdiv((uint32_t)cpr), (uint32_t)threads);
+                       make_fastdiv((uint32_t)cpr), (uint32_t)threads, (uint32_t)chunks);
     nscales = rows * (cols / 16);
   } else {
     hipLaunchKernelGGL(msedn_pass1_col, dim3((unsigned)(rows / 128), (unsigned)((cols + 63) / 64)),
