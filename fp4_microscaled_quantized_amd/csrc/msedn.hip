@@ -296,10 +296,11 @@ __global__ __launch_bounds__(256) void msedn_pass1_row(
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1, column axis: 128 x 64 bf16 tile in LDS; quad = one column's chunk.
+// Pass 1, column axis: 128 x 128 bf16 tile in LDS; a quad takes one pair of
+// adjacent columns (one 4-byte LDS read gives both), i.e. two output chunks.
 // Output operand row = input column, output column = input row.
 // ---------------------------------------------------------------------------
-constexpr int kCPitch = 132;  // bytes per LDS row: 2-way conflicts between quads at most
+constexpr int kCPitch = 260;  // bytes per LDS row: 2-way conflicts between quads at most
 
 __global__ __launch_bounds__(256) void msedn_pass1_col(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, Mask128 mask,
@@ -307,12 +308,12 @@ __global__ __launch_bounds__(256) void msedn_pass1_col(
     float* __restrict__ eden_s, uint32_t* __restrict__ gmax) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kCPitch];
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 128, cb = (int64_t)blockIdx.y * 64;
-  const int nc = (int)min<int64_t>(64, cols - cb);
+  const int64_t r0 = (int64_t)blockIdx.x * 128, cb = (int64_t)blockIdx.y * 128;
+  const int nc = (int)min<int64_t>(128, cols - cb);
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int id = tid + 256 * it;  // 1024 chunks of 8 bf16
-    const int r = id >> 3, chk = id & 7;
+  for (int it = 0; it < 8; ++it) {
+    const int id = tid + 256 * it;  // 2048 chunks of 8 bf16
+    const int r = id >> 4, chk = id & 15;
     if (chk * 8 < nc) {
       const u32x4 v = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4*>(x + (r0 + r) * ld + cb + chk * 8));
@@ -321,35 +322,46 @@ __global__ __launch_bounds__(256) void msedn_pass1_col(
     }
   }
   __syncthreads();
-  const int c = tid >> 2, l4 = tid & 3;
-  const bool live = c < nc;
-  const int cc = live ? c : 0;
-  float tv[32];
-  const uint32_t m = mask.w[l4];
+  const int cp = tid >> 2, l4 = tid & 3;
+  const bool live = 2 * cp < nc;  // nc is a multiple of 32: both columns or neither
+  const int cc = live ? cp : 0;
+  uint32_t wpair[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t h = *reinterpret_cast<const uint16_t*>(tile + (32 * l4 + i) * kCPitch + 2 * cc);
-    tv[i] = __uint_as_float((h << 16) ^ (((m >> i) & 1u) << 31));
+  for (int i = 0; i < 32; ++i)
+    wpair[i] = *reinterpret_cast<const uint32_t*>(tile + (32 * l4 + i) * kCPitch + 4 * cc);
+  const uint32_t m = mask.w[l4];
+  float vmax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float tv[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t b = k == 0 ? wpair[i] << 16 : wpair[i] & 0xFFFF0000u;
+      tv[i] = __uint_as_float(b ^ (((m >> i) & 1u) << 31));
+    }
+    uint32_t cw[4];
+    float v[2], S;
+    msedn_core(tv, l4, clip_s, cw, v, S);
+    if (live) {
+      const int64_t orow = cb + 2 * cp + k, ocol = r0 + 32 * l4;
+      *reinterpret_cast<u32x4*>(codes + orow * (rows / 2) + ocol / 2) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+      *reinterpret_cast<float2*>(vbuf + orow * (rows / 16) + ocol / 16) = make_float2(v[0], v[1]);
+      if (eden_s && l4 == 0) eden_s[orow * (rows / 128) + r0 / 128] = S;
+      vmax = fmaxf(vmax, fmaxf(v[0], v[1]));
+    }
   }
-  uint32_t cw[4];
-  float v[2], S;
-  msedn_core(tv, l4, clip_s, cw, v, S);
-  if (live) {
-    const int64_t orow = cb + c, ocol = r0 + 32 * l4;
-    *reinterpret_cast<u32x4*>(codes + orow * (rows / 2) + ocol / 2) = u32x4{cw[0], cw[1], cw[2], cw[3]};
-    *reinterpret_cast<float2*>(vbuf + orow * (rows / 16) + ocol / 16) = make_float2(v[0], v[1]);
-    if (eden_s && l4 == 0) eden_s[orow * (rows / 128) + r0 / 128] = S;
-  }
-  block_max_atomic(live ? fmaxf(v[0], v[1]) : 0.0f, gmax);
+  block_max_atomic(vmax, gmax);
 }
 
 // ---------------------------------------------------------------------------
 // Pass 1 on a saved NVFP4 operand (the backward's re-quantization of the
-// forward's Q(X), Q(W)): a 128 x 64 tile of codes and E4M3 scales is decoded
-// to fp32 values fl(fl(q * s16) * g) in LDS (q * s16 is exact), then each quad
-// takes one column's 128-chunk as above.  Output row = input column.
+// forward's Q(X), Q(W)): the codes and E4M3 scales of a 128 x 128 tile are
+// staged in LDS as they are (9 KB); a quad takes a pair of adjacent columns,
+// whose codes share one byte per row, and decodes fl(fl(q * s16) * g) as it
+// reads (q * s16 is exact).  Output row = input column.
 // ---------------------------------------------------------------------------
-constexpr int kFPitch = 65;  // floats per LDS row: 2-way conflicts between quads at most
+constexpr int kNCodePitch = 68;   // code bytes per LDS row (64 + pad)
+constexpr int kNScalePitch = 12;  // scale bytes per LDS row (8 + pad)
 
 // OCP E4M3FN byte -> float (exact); 0x7F / 0xFF are NaN.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
@@ -364,54 +376,64 @@ __global__ __launch_bounds__(256) void msedn_pass1_col_nv(
     const float* __restrict__ qg, int64_t rows, int64_t cols, Mask128 mask, float clip_s,
     uint8_t* __restrict__ codes, float* __restrict__ vbuf, float* __restrict__ eden_s,
     uint32_t* __restrict__ gmax) {
-  __shared__ float tile[128 * kFPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t tcodes[128 * kNCodePitch];
+  __shared__ __attribute__((aligned(16))) uint8_t tscales[128 * kNScalePitch];
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 128, cb = (int64_t)blockIdx.y * 64;
-  const int nc = (int)min<int64_t>(64, cols - cb);
+  const int64_t r0 = (int64_t)blockIdx.x * 128, cb = (int64_t)blockIdx.y * 128;
+  const int nc = (int)min<int64_t>(128, cols - cb);  // a multiple of 32
   {
-    // thread = 32 consecutive elements of one source row: row tid/2, half tid&1
-    const int r = tid >> 1, h = tid & 1;
-    if (h * 32 < nc) {
-      const int64_t row = r0 + r, c0 = cb + 32 * h;
-      const float g = *qg;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qcodes + row * (cols / 2) + c0 / 2);
-      const uint32_t sw = *reinterpret_cast<const uint16_t*>(qscales + row * (cols / 16) + c0 / 16);
-      const float s0 = e4m3_to_f32(sw & 0xFFu), s1 = e4m3_to_f32(sw >> 8);
-      const uint32_t cw[4] = {v.x, v.y, v.z, v.w};
-      float* d = tile + r * kFPitch + 32 * h;
+    // codes: 128 rows x 64 bytes = 512 chunks of 16 B, two per thread
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float qv[8];
-        e2m1_pair<0>(cw[w], qv[0], qv[1]);
-        e2m1_pair<1>(cw[w], qv[2], qv[3]);
-        e2m1_pair<2>(cw[w], qv[4], qv[5]);
-        e2m1_pair<3>(cw[w], qv[6], qv[7]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) d[8 * w + i] = (qv[i] * (w < 2 ? s0 : s1)) * g;
+    for (int it = 0; it < 2; ++it) {
+      const int id = tid + 256 * it;
+      const int r = id >> 2, chk = id & 3;
+      if (chk * 32 < nc) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qcodes + (r0 + r) * (cols / 2) + cb / 2 + chk * 16);
+        uint32_t* d = reinterpret_cast<uint32_t*>(tcodes + r * kNCodePitch + chk * 16);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
       }
     }
+    // scales: 128 rows x 8 bytes, thread = 4 bytes (two 2-byte loads) of one row
+    const int r = tid >> 1, h = tid & 1;
+    const uint8_t* sp = qscales + (r0 + r) * (cols / 16) + cb / 16 + 4 * h;
+    uint16_t* sd = reinterpret_cast<uint16_t*>(tscales + r * kNScalePitch + 4 * h);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if ((4 * h + 2 * u) * 16 < nc) sd[u] = *reinterpret_cast<const uint16_t*>(sp + 2 * u);
   }
   __syncthreads();
-  const int c = tid >> 2, l4 = tid & 3;
-  const bool live = c < nc;
-  const int cc = live ? c : 0;
-  float tv[32];
+  const int cp = tid >> 2, l4 = tid & 3;
+  const bool live = 2 * cp < nc;  // both columns of the pair or neither
+  const int cc = live ? cp : 0;
+  const float g = *qg;
   const uint32_t m = mask.w[l4];
+  float ta[32], tb[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const float x = tile[(32 * l4 + i) * kFPitch + cc];
-    tv[i] = __uint_as_float(__float_as_uint(x) ^ (((m >> i) & 1u) << 31));
+    const int row = 32 * l4 + i;
+    const uint32_t byte = tcodes[row * kNCodePitch + cc];
+    const float s16 = e4m3_to_f32(tscales[row * kNScalePitch + (cc >> 3)]);
+    float qa, qb;
+    e2m1_pair<0>(byte, qa, qb);
+    const uint32_t flip = ((m >> i) & 1u) << 31;
+    ta[i] = __uint_as_float(__float_as_uint((qa * s16) * g) ^ flip);
+    tb[i] = __uint_as_float(__float_as_uint((qb * s16) * g) ^ flip);
   }
-  uint32_t cw[4];
-  float v[2], S;
-  msedn_core(tv, l4, clip_s, cw, v, S);
-  if (live) {
-    const int64_t orow = cb + c, ocol = r0 + 32 * l4;
-    *reinterpret_cast<u32x4*>(codes + orow * (rows / 2) + ocol / 2) = u32x4{cw[0], cw[1], cw[2], cw[3]};
-    *reinterpret_cast<float2*>(vbuf + orow * (rows / 16) + ocol / 16) = make_float2(v[0], v[1]);
-    if (eden_s && l4 == 0) eden_s[orow * (rows / 128) + r0 / 128] = S;
+  float vmax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    uint32_t cw[4];
+    float v[2], S;
+    msedn_core(k == 0 ? ta : tb, l4, clip_s, cw, v, S);
+    if (live) {
+      const int64_t orow = cb + 2 * cp + k, ocol = r0 + 32 * l4;
+      *reinterpret_cast<u32x4*>(codes + orow * (rows / 2) + ocol / 2) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+      *reinterpret_cast<float2*>(vbuf + orow * (rows / 16) + ocol / 16) = make_float2(v[0], v[1]);
+      if (eden_s && l4 == 0) eden_s[orow * (rows / 128) + r0 / 128] = S;
+      vmax = fmaxf(vmax, fmaxf(v[0], v[1]));
+    }
   }
-  block_max_atomic(live ? fmaxf(v[0], v[1]) : 0.0f, gmax);
+  block_max_atomic(vmax, gmax);
 }
 
 // ---------------------------------------------------------------------------
@@ -469,7 +491,7 @@ hipError_t launch_msedn_requant(const uint8_t* qcodes, const uint8_t* qscales, c
   msedn_sign_words(seed, gemm_id, m.w);
   const RngKey key = make_key(seed, stream);
   hipLaunchKernelGGL(msedn_zero, dim3(1), dim3(1), 0, s, gmax);
-  hipLaunchKernelGGL(msedn_pass1_col_nv, dim3((unsigned)(rows / 128), (unsigned)((cols + 63) / 64)),
+  hipLaunchKernelGGL(msedn_pass1_col_nv, dim3((unsigned)(rows / 128), (unsigned)((cols + 127) / 128)),
                      dim3(256), 0, s, qcodes, qscales, qg, rows, cols, m, clip_s, codes, vbuf,
                      eden_s, gmax);
   const int64_t nscales = cols * (rows / 16);
@@ -503,7 +525,7 @@ hipError_t launch_msedn(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
                        make_fastdiv((uint32_t)cpr), (uint32_t)threads, (uint32_t)chunks);
     nscales = rows * (cols / 16);
   } else {
-    hipLaunchKernelGGL(msedn_pass1_col, dim3((unsigned)(rows / 128), (unsigned)((cols + 63) / 64)),
+    hipLaunchKernelGGL(msedn_pass1_col, dim3((unsigned)(rows / 128), (unsigned)((cols + 127) / 128)),
                        dim3(256), 0, s, x, rows, cols, ld, m, clip_s, codes, vbuf, eden_s, gmax);
     nscales = cols * (rows / 16);
   }
