@@ -513,7 +513,7 @@ def time_quartet2(steps, warmup):
     return res
 
 
-def cpu_baseline(rows=256):
+def cpu_baseline(rows=1024):
     """The oracle's linear fwd+bwd on the first `rows` tokens of the headline workload."""
     from fp4_microscaled_quantized_amd import synth
     from oracle import mx, rng
