@@ -163,9 +163,9 @@ class LinearStep(_Step):
 
 
 class QuestStep(_Step):
-    """QuEST forward + the Quartet backward in the forward-rotated basis as ten
+    """QuEST forward + the Quartet backward in the forward-rotated basis as eight
     C-ABI launches: QuEST X, QuEST W, GEMM Y, dual SR quant dY, re-quantize
-    W_q and X_q, GEMM dX, mask + inverse RHT dX, GEMM dW, mask + inverse RHT dW."""
+    W_q and X_q, GEMM dX and GEMM dW with the mask + inverse-RHT epilogue."""
 
     def __init__(self, d, seed=0):
         import torch
@@ -185,8 +185,8 @@ class QuestStep(_Step):
         f = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
         self.y, self.dx, self.dw = f(m, n), f(m, k), f(n, k)
         self.g = [fq.sign_mask(seed, i) for i in range(3)]
-        self.names = ["quest_x", "quest_w", "gemm_y", "quant_dy", "requant_w", "requant_x", "gemm_dx",
-                      "unmask_dx", "gemm_dw", "unmask_dw"]
+        self.names = ["quest_x", "quest_w", "gemm_y", "quant_dy", "requant_w", "requant_x",
+                      "gemm_dx_irht", "gemm_dw_irht"]
         self.times = {nm: [] for nm in self.names}
 
     def _calls(self):
@@ -212,12 +212,11 @@ class QuestStep(_Step):
                                               _ptr(self.wtq), _ptr(self.wts), s)),
             lambda: _check(L.fp4mx_requantize(_ptr(self.xq), _ptr(self.xs), m, k, SR, g2, seed, 4,
                                               _ptr(self.xtq), _ptr(self.xts), s)),
-            lambda: _check(L.fp4mx_gemm(_ptr(self.dq), _ptr(self.ds), _ptr(self.wtq), _ptr(self.wts), m, k, n,
-                                        a, _ptr(self.dx), k, s)),
-            lambda: _check(L.fp4mx_unmask_inverse_hadamard(_ptr(self.dx), m, k, k, _ptr(self.xm), g0, s)),
-            lambda: _check(L.fp4mx_gemm(_ptr(self.dtq), _ptr(self.dts), _ptr(self.xtq), _ptr(self.xts), n, k, m,
-                                        a, _ptr(self.dw), k, s)),
-            lambda: _check(L.fp4mx_unmask_inverse_hadamard(_ptr(self.dw), n, k, k, _ptr(self.wm), g0, s)),
+            lambda: _check(L.fp4mx_gemm_unmask_irht(_ptr(self.dq), _ptr(self.ds), _ptr(self.wtq), _ptr(self.wts),
+                                                    m, k, n, a, _ptr(self.dx), k, _ptr(self.xm), g0, s)),
+            lambda: _check(L.fp4mx_gemm_unmask_irht(_ptr(self.dtq), _ptr(self.dts), _ptr(self.xtq),
+                                                    _ptr(self.xts), n, k, m, a, _ptr(self.dw), k, _ptr(self.wm),
+                                                    g0, s)),
         ]
 
     def check_against_composite(self):
@@ -250,21 +249,21 @@ def time_step(st, steps, warmup):
 
 
 def time_quest(steps, warmup):
-    """The QuEST layer on the Quartet workload: step rate and each kernel
+    """The QuEST layer on the Quartet workload: step rate and each quantizer
     against its roofline (algorithmic bytes: QuEST 2 + 0.5 + 1/32 + 1/8 B per
-    element, re-quantizer 2 x 0.53125, mask + inverse RHT 4 + 1/8 + 4)."""
+    element, re-quantizer 2 x 0.53125)."""
     from fp4_microscaled_quantized_amd import synth
     st = QuestStep(synth.quartet_linear(0))
     wall, avg, _ = time_step(st, steps, warmup)
     ms = wall * 1e3 / steps
     m, n, k = st.m, st.n, st.k
     by = {"quest_x": m * k * (2 + 0.5 + 1 / 32 + 1 / 8), "quest_w": n * k * (2 + 0.5 + 1 / 32 + 1 / 8),
-          "requant_w": n * k * 2 * (0.5 + 1 / 32), "requant_x": m * k * 2 * (0.5 + 1 / 32),
-          "unmask_dx": m * k * (8 + 1 / 8), "unmask_dw": n * k * (8 + 1 / 8)}
+          "requant_w": n * k * 2 * (0.5 + 1 / 32), "requant_x": m * k * 2 * (0.5 + 1 / 32)}
     kr = {nm: {"GB/s": round(b / (avg[nm] * 1e-3) / 1e9, 1),
                "frac_hbm": round(b / (avg[nm] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)} for nm, b in by.items()}
-    gemm_ms = avg["gemm_y"] + avg["gemm_dx"] + avg["gemm_dw"]
-    return {"workload": "QuEST fwd + Quartet bwd (rotated basis, masks, inverse RHT) M=8192 N=K=4096",
+    gemm_ms = avg["gemm_y"] + avg["gemm_dx_irht"] + avg["gemm_dw_irht"]
+    return {"workload": "QuEST fwd + Quartet bwd (rotated basis; masks and inverse RHT in the GEMM epilogue) "
+                        "M=8192 N=K=4096",
             "ms_per_step": round(ms, 4), "TFLOP/s": round(st.flops() / (ms * 1e-3) / 1e12, 1),
             "gemm_TFLOP/s": round(6.0 * m * n * k / (gemm_ms * 1e-3) / 1e12, 1),
             "breakdown_ms": {nm: round(v, 4) for nm, v in avg.items()}, "kernel_hbm": kr}

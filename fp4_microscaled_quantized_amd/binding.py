@@ -62,6 +62,7 @@ _SIGS = {
     "fp4mx_quest_quantize": (_INT, [_P, _I64, _I64, _I64, C.c_float, _U32, _P, _P, _P, _P]),
     "fp4mx_requantize": (_INT, [_P, _P, _I64, _I64, _INT, _U32, _U64, _U32, _P, _P, _P]),
     "fp4mx_unmask_inverse_hadamard": (_INT, [_P, _I64, _I64, _I64, _P, _U32, _P]),
+    "fp4mx_gemm_unmask_irht": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, C.c_float, _P, _I64, _P, _U32, _P]),
     "fp4mx_quest_ctx_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4mx_quest_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4mx_quest_linear_fwd": (_INT, [_P, _P, _I64, _I64, _I64, C.c_float, _U64, _P,
@@ -271,6 +272,18 @@ def unmask_inverse_hadamard(c, clip_mask, mask=0):
         raise ValueError("c must be a row-major fp32 matrix")
     _check(lib().fp4mx_unmask_inverse_hadamard(_ptr(c), c.shape[0], c.shape[1], c.stride(0),
                                                _ptr(clip_mask), mask, _stream(c.device)))
+    return c
+
+
+def gemm_unmask_irht(a: MXTensor, b: MXTensor, clip_mask, alpha: float = 1.0, mask=0, out=None):
+    """C = H^-1((alpha deq(A) deq(B)^T) with clipped entries zeroed), fp32, in one kernel."""
+    m, n, k = a.codes.shape[0], b.codes.shape[0], a.codes.shape[1] * 2
+    if b.codes.shape[1] * 2 != k:
+        raise ValueError("inner dimensions differ")
+    c = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=a.codes.device)
+    _check(lib().fp4mx_gemm_unmask_irht(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), m,
+                                        n, k, alpha, _ptr(c), c.stride(0), _ptr(clip_mask), mask,
+                                        _stream(c.device)))
     return c
 
 

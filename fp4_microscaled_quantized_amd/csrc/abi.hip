@@ -290,6 +290,20 @@ int fp4mx_unmask_inverse_hadamard(float* c, int64_t rows, int64_t cols, int64_t 
   return e == hipSuccess ? FP4MX_OK : hip_fail(e);
 }
 
+int fp4mx_gemm_unmask_irht(const uint8_t* a_codes, const uint8_t* a_scales,
+                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t m, int64_t n,
+                           int64_t k, float alpha, float* c, int64_t ldc, const uint8_t* mask,
+                           uint32_t sign_mask, void* stream) {
+  int st = check_gemm_args(a_codes, a_scales, b_codes, b_scales, m, n, k, c, ldc);
+  if (st) return st;
+  if (!mask) return FP4MX_E_NULL;
+  if (!aligned4(mask)) return FP4MX_E_ALIGN;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_mx_gemm_irht(a_codes, a_scales, b_codes, b_scales, m, n, k, alpha, c, ldc,
+                                     mask, sign_mask, (hipStream_t)stream);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
 size_t fp4mx_quest_ctx_bytes(int64_t m, int64_t n, int64_t k) {
   if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
   return mx_bytes(m, k) + mx_bytes(n, k) + round_up((size_t)m * k / 8) + round_up((size_t)n * k / 8);
@@ -368,10 +382,10 @@ int fp4mx_quest_linear_bwd(const void* dy, const fp4mx_quest_ctx* ctx, int64_t m
   if (e == hipSuccess)
     e = launch_requant(ctx->xq_codes, ctx->xq_scales, m, k, FP4MX_ROUND_SR, g2, make_key(seed, 4),
                        xtq, xts, s);
-  if (e == hipSuccess) e = launch_mx_gemm(dq, ds, wtq, wts, m, k, n, alpha, dx, k, s);
-  if (e == hipSuccess) e = launch_unmask_irht(dx, m, k, k, ctx->x_mask, g0, s);
-  if (e == hipSuccess) e = launch_mx_gemm(tq, ts, xtq, xts, n, k, m, alpha, dw, k, s);
-  if (e == hipSuccess) e = launch_unmask_irht(dw, n, k, k, ctx->w_mask, g0, s);
+  if (e == hipSuccess)
+    e = launch_mx_gemm_irht(dq, ds, wtq, wts, m, k, n, alpha, dx, k, ctx->x_mask, g0, s);
+  if (e == hipSuccess)
+    e = launch_mx_gemm_irht(tq, ts, xtq, xts, n, k, m, alpha, dw, k, ctx->w_mask, g0, s);
   return e == hipSuccess ? FP4MX_OK : hip_fail(e);
 }
 

@@ -76,6 +76,14 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, int64_t r
 hipError_t launch_unmask_irht(float* c, int64_t rows, int64_t cols, int64_t ldc,
                               const uint8_t* mask, uint32_t sign_mask, hipStream_t s);
 
+// FP4 GEMM whose epilogue zeroes the entries masked in cmask ([m][n/32] words,
+// bit j = column 32g + j) and applies the inverse block-32 RHT (sign_mask)
+// along each row of C.
+hipError_t launch_mx_gemm_irht(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                               const uint8_t* bs, int64_t m, int64_t n, int64_t k, float alpha,
+                               float* c, int64_t ldc, const uint8_t* cmask, uint32_t sign_mask,
+                               hipStream_t s);
+
 // MS-EDEN, two passes (csrc/msedn.hip).  vbuf: fp32 per output 16-group;
 // gmax: one uint32 (global max of vbuf).
 hipError_t launch_msedn(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int axis,

@@ -230,6 +230,19 @@ FP4MX_API int fp4mx_requantize(const uint8_t* codes, const uint8_t* scales, int6
 FP4MX_API int fp4mx_unmask_inverse_hadamard(float* c, int64_t rows, int64_t cols, int64_t ldc,
                                   const uint8_t* mask, uint32_t sign_mask, void* stream);
 
+/* fp4mx_gemm followed by fp4mx_unmask_inverse_hadamard on its output, in one
+ * kernel: C = H^-1((alpha * deq(A) deq(B)^T) with the entries masked in
+ * `mask` zeroed), per 32-column group of each row of C, H^-1 inverting the
+ * forward RHT with sign_mask.  mask: uint8 [m][n/8] (4-B aligned), layout and
+ * sense as above.  The transform runs in the GEMM's epilogue (C never takes
+ * the intermediate value), with the same fp32 operations in the same order as
+ * the two-call form, so the results are identical.  Errors as fp4mx_gemm;
+ * E_NULL for a null mask, E_ALIGN for a misaligned one. */
+FP4MX_API int fp4mx_gemm_unmask_irht(const uint8_t* a_codes, const uint8_t* a_scales,
+                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t m, int64_t n,
+                           int64_t k, float alpha, float* c, int64_t ldc, const uint8_t* mask,
+                           uint32_t sign_mask, void* stream);
+
 /* Saved QuEST forward context: X_q [m][k] (codes, scales), W_q [n][k], the
  * clipping masks M_x [m][k/8] and M_w [n][k/8], and the seed.  Caller-owned
  * device memory; fp4mx_quest_ctx_bytes gives the total of the six buffers. */

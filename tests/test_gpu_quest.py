@@ -219,3 +219,30 @@ def test_quest_linear_full_size_sampled():
     edw = rel_fro(dw[np.ix_(cj, ck)], rdw)
     log("  sampled rel err y %.2e dx %.2e dw %.2e" % (ey, edx, edw))
     assert ey <= TOL and edx <= TOL and edw <= TOL
+
+
+@pytest.mark.parametrize("m,n,k,ldc", [(256, 256, 128, 256), (352, 160, 96, 160), (96, 544, 256, 576)])
+def test_gemm_unmask_irht_fused(m, n, k, ldc):
+    """The GEMM with the mask + inverse-RHT epilogue equals fp4mx_gemm followed
+    by fp4mx_unmask_inverse_hadamard bit for bit, and the oracle within 1e-5."""
+    log("gemm unmask irht", m, n, k, ldc)
+    rs = np.random.default_rng(m + n)
+    a = mx.quantize(host_f32(synth.normal((m, k), 1.0, 9, 0)), rounding=mx.SR, sign_mask=3, seed=2, stream=1)
+    b = mx.quantize(host_f32(synth.normal((n, k), 1.0, 9, 1)), rounding=mx.SR, sign_mask=3, seed=2, stream=2)
+    bits = rs.random((m, n)) < 0.05
+    mk = np.packbits(bits, axis=1, bitorder="little")
+    sm = rng.sign_mask(9, 0)
+    A = fq.MXTensor(torch.from_numpy(a[0]).cuda(), torch.from_numpy(a[1]).cuda())
+    B = fq.MXTensor(torch.from_numpy(b[0]).cuda(), torch.from_numpy(b[1]).cuda())
+    dmk = torch.from_numpy(mk).cuda()
+    c1 = torch.full((m, ldc), 7.0, dtype=torch.float32, device="cuda")
+    fq.gemm_unmask_irht(A, B, dmk, alpha=16 / 9, mask=sm, out=c1[:, :n])
+    c2 = torch.full((m, ldc), 7.0, dtype=torch.float32, device="cuda")
+    fq.gemm(A, B, alpha=16 / 9, out=c2[:, :n])
+    fq.unmask_inverse_hadamard(c2[:, :n], dmk, mask=sm)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    want = quest.unmask_inverse_rht(mx.gemm(*a, *b, alpha=mx.ALPHA_BWD), mk, sm)
+    got = cpu(c1)
+    assert rel_fro(got[:, :n], want) <= TOL
+    assert np.all(got[:, n:] == 7.0)                     # padding columns untouched
