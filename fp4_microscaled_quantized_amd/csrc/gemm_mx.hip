@@ -103,8 +103,13 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint8_t* lds, uint32_t 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
 }
+// C stores are non-temporal (cache policy nt): the output is written once
+// and is far larger than L2, and letting it allocate evicts the operand
+// panels that later tiles re-read (measured: 8192x14336x4096 GEMM 315 ->
+// 285 us; no change at 8192x4096x4096).
+constexpr int kStoreNT = 2;
 __device__ __forceinline__ void buf_store4(float v, rsrc_t r, uint32_t off) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, kStoreNT);
 }
 
 template <int FMT>
@@ -450,7 +455,7 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
         const uint32_t bad = 0u - (uint32_t)(col >= N);
         const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 4u) & ~bad) | (kOOB & bad);
         __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, w), rC, (int)off, 0, 0);
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, w), rC, (int)off, 0, kStoreNT);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // this block's reads are done before it is overwritten
       __builtin_amdgcn_wave_barrier();
