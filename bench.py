@@ -418,6 +418,36 @@ def _time_calls(call, steps, warmup):
     return ev[0].elapsed_time(ev[1]) / steps
 
 
+def time_gemm_outputs(steps, warmup, rounds=3):
+    """The MXFP4 GEMM with fp32 output against the bf16-output variant
+    (fp4mx_gemm_bf16), per launch, on the Quartet and Llama FFN-up shapes.
+    The two are timed alternately, `rounds` times each; medians reported."""
+    import torch
+    import fp4_microscaled_quantized_amd as fq
+    res = {"workload": "MXFP4 GEMM per launch, fp32 vs bf16 output (random codes, E8M0 scales 2^-9..2^2)"}
+    for (m, n, k) in [(8192, 4096, 4096), (8192, 14336, 4096)]:
+        g = torch.Generator(device="cuda").manual_seed(5)
+
+        def op(r):
+            return fq.MXTensor(torch.randint(0, 256, (r, k // 2), dtype=torch.uint8, device="cuda", generator=g),
+                               torch.randint(118, 130, (r, k // 32), dtype=torch.uint8, device="cuda", generator=g))
+        A, B = op(m), op(n)
+        c32 = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        c16 = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        t32, t16 = [], []
+        for _ in range(rounds):
+            t32.append(_time_calls(lambda i: fq.gemm(A, B, out=c32), steps, warmup))
+            t16.append(_time_calls(lambda i: fq.gemm_bf16(A, B, out=c16), steps, warmup))
+        t32, t16 = float(np.median(t32)), float(np.median(t16))
+        fl = 2.0 * m * n * k
+        res["%dx%dx%d" % (m, n, k)] = {"fp32_out_us": round(t32 * 1e3, 1), "bf16_out_us": round(t16 * 1e3, 1),
+                                        "fp32_out_TFLOP/s": round(fl / (t32 * 1e-3) / 1e12, 1),
+                                        "bf16_out_TFLOP/s": round(fl / (t16 * 1e-3) / 1e12, 1)}
+        del A, B, c32, c16
+        torch.cuda.empty_cache()
+    return res
+
+
 def time_nvfp4_bwd(steps, warmup):
     """NVFP4 backward with MS-EDEN operands on the Quartet layer (dX and dW,
     4 MS-EDEN quantizations + 2 FP8-staged GEMMs), and the unbiased quantizers
@@ -589,6 +619,8 @@ def main():
                                    "breakdown_ms": {k2: round(v, 4) for k2, v in avg2.items()}}
             del st2
             torch.cuda.empty_cache()
+        out["gemm_output_dtype"] = time_gemm_outputs(max(a.steps // 2, 20), 10)
+        torch.cuda.empty_cache()
         out["quantizer"] = time_quantizer(max(a.steps, 20), a.warmup)
         torch.cuda.empty_cache()
         out["nvfp4"] = time_nvfp4(max(a.steps // 2, 5), 2)

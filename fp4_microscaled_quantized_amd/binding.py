@@ -55,6 +55,7 @@ _SIGS = {
     "fp4mx_hadamard_quantize_dual": (_INT, [_P, _I64, _I64, _I64, _INT, _U32, _U32, _INT, _U32, _U32,
                                             _U64, _P, _P, _P, _P, _P]),
     "fp4mx_gemm": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, C.c_float, _P, _I64, _P]),
+    "fp4mx_gemm_bf16": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, C.c_float, _P, _I64, _P]),
     "fp4mx_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4mx_ctx_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4mx_linear_fwd": (_INT, [_P, _P, _I64, _I64, _I64, _U64, _P, C.POINTER(CtxStruct), _P, _SZ, _P]),
@@ -189,6 +190,19 @@ def gemm(a: MXTensor, b: MXTensor, alpha: float = 1.0, out: torch.Tensor | None 
     c = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=a.codes.device)
     _check(lib().fp4mx_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), m, n, k,
                             alpha, _ptr(c), c.stride(0), _stream(c.device)))
+    return c
+
+
+def gemm_bf16(a: MXTensor, b: MXTensor, alpha: float = 1.0, out: torch.Tensor | None = None):
+    """C = bf16_RNE(alpha * deq(A) deq(B)^T) from the fp32 accumulation."""
+    m, n, k = a.codes.shape[0], b.codes.shape[0], a.codes.shape[1] * 2
+    if b.codes.shape[1] * 2 != k:
+        raise ValueError("inner dimensions differ")
+    c = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=a.codes.device)
+    if c.dtype != torch.bfloat16:
+        raise TypeError("out must be bfloat16")
+    _check(lib().fp4mx_gemm_bf16(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), m, n,
+                                 k, alpha, _ptr(c), c.stride(0), _stream(c.device)))
     return c
 
 

@@ -167,6 +167,19 @@ int fp4mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b
   return e == hipSuccess ? FP4MX_OK : hip_fail(e);
 }
 
+int fp4mx_gemm_bf16(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                    const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, float alpha,
+                    uint16_t* c, int64_t ldc, void* stream) {
+  int st = check_gemm_args(a_codes, a_scales, b_codes, b_scales, m, n, k,
+                           reinterpret_cast<const float*>(c), ldc);
+  if (st) return st;
+  if (ldc % 8 != 0) return FP4MX_E_ALIGN;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_mx_gemm_bf16(a_codes, a_scales, b_codes, b_scales, m, n, k, alpha, c, ldc,
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
 size_t fp4mx_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return 0;
   const size_t fwd = mx_bytes(m, k) + mx_bytes(n, k);

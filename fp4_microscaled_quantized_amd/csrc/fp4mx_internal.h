@@ -83,6 +83,9 @@ hipError_t launch_mx_gemm_irht(const uint8_t* a, const uint8_t* as, const uint8_
                                const uint8_t* bs, int64_t m, int64_t n, int64_t k, float alpha,
                                float* c, int64_t ldc, const uint8_t* cmask, uint32_t sign_mask,
                                hipStream_t s);
+hipError_t launch_mx_gemm_bf16(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                               const uint8_t* bs, int64_t m, int64_t n, int64_t k, float alpha,
+                               uint16_t* c, int64_t ldc, hipStream_t s);
 
 // MS-EDEN, two passes (csrc/msedn.hip).  vbuf: fp32 per output 16-group;
 // gmax: one uint32 (global max of vbuf).

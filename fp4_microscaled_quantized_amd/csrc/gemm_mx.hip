@@ -3,7 +3,8 @@
 //
 // Computes C = alpha * deq(A) deq(B)^T with A [m][k], B [n][k] stored K-major
 // (FP4: two codes per byte; FP8: one per byte) and one E8M0 scale per 32 K
-// elements per row; fp32 accumulation and output.
+// elements per row; fp32 accumulation; fp32 output, or bf16 (RNE of the
+// fp32 result) for the bf16-output entry point.
 // Source: "Quartet: Native FP4 Training Can Be Optimal for Large Language
 // Models" -- "The GPU Kernel Implementation", Stage 2 (block-scaled GEMM
 // D = C + (A x SFA)(B x SFB), FP32 accumulator and output).
@@ -23,12 +24,13 @@
 //    current substep's MFMAs issue.
 //  - Global traffic uses buffer resources: out-of-range rows and K chunks
 //    read as zero in hardware, so there are no branches around loads.
-//  - LDS rows are padded to 144 B (the 16-B fragment reads of 8 consecutive
-//    rows hit distinct banks); each row's stage scales are stored as two
-//    dwords holding groups {h, 2+h, 4+h, 6+h}, byte s selected by op_sel.
-//  - Optional epilogue for the Quartet backward in the forward-rotated basis:
-//    C <- H^-1((alpha acc) with masked entries zeroed) per 32-column group,
-//    through LDS staging (the stage buffers are free after the last stage).
+//  - LDS rows are XOR-swizzled in 16-B chunks (conflict-free fragment
+//    reads); each row's stage scales are stored as two dwords holding
+//    groups {h, 2+h, 4+h, 6+h}, byte s selected by op_sel.
+//  - Epilogues: fp32 stores straight from the accumulators; or, through LDS
+//    staging (the stage buffers are free after the last stage), the Quartet
+//    backward's C <- H^-1((alpha acc) with masked entries zeroed) per
+//    32-column group, or a bf16 output with whole-row 16-B stores.
 //  - Tiles are assigned XCD-aware: workgroup i runs on XCD i % 8, so each XCD
 //    gets a contiguous run of tiles in grouped (4 tile-rows) order and shares
 //    A and B panels in its own L2.
@@ -112,6 +114,19 @@ __device__ __forceinline__ void buf_store4(float v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, kStoreNT);
 }
 
+// Epilogue kinds.
+constexpr int kEpiF32 = 0;   // C fp32
+constexpr int kEpiIrht = 1;  // C fp32 <- H^-1(mask-zeroed alpha acc) per 32-column group
+constexpr int kEpiBf16 = 2;  // C bf16 = RNE(alpha acc)
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.  Written as
+// a select: an early return for NaN compiles to a branch per element.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
+}
+
 template <int FMT>
 struct Fmt {
   static constexpr int kStageK = FMT == 4 ? 256 : 128;  // K elements per stage
@@ -134,7 +149,7 @@ __device__ __forceinline__ void tile_of(int wg, int gm, int gn, int& tm, int& tn
   tn = r / gsz;
 }
 
-template <int FMT, bool VEC, int WM, int WN, bool IRHT>
+template <int FMT, bool VEC, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, int M, int N, int K, float alpha,
@@ -364,8 +379,10 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
 
   // ---- epilogue: lane l, reg v -> row 8(v/4) + 4(l/32) + v%4, col l%32 ----
   const int rowsC = min(kBM, M - m0);
-  const rsrc_t rC = make_rsrc(C + (size_t)m0 * ldc, (uint32_t)rowsC * (uint32_t)ldc * 4u);
-  if constexpr (!IRHT) {
+  constexpr uint32_t kCB = EPI == kEpiBf16 ? 2u : 4u;  // bytes per C element
+  const rsrc_t rC = make_rsrc(reinterpret_cast<uint8_t*>(C) + (size_t)m0 * ldc * kCB,
+                              (uint32_t)rowsC * (uint32_t)ldc * kCB);
+  if constexpr (EPI == kEpiF32) {
     // straight from the accumulators: per instruction two 128-B row pieces
     // (measured faster here than staging through LDS for whole-row stores)
 #pragma unroll
@@ -383,19 +400,20 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
       }
     }
   } else {
-    // IRHT: C <- H^-1((alpha acc) with masked entries zeroed) per 32-column
-    // group, H^-1 y = s o (c FWHT(y)).  The stage buffers are free after the
-    // last barrier: each wave stages one 32-row block of its sub-tile at a
-    // time (32 x 128 fp32, row pitch 132 floats); every lane takes two whole
-    // 32-column groups of it, transforms them in registers and puts them
-    // back, and the wave stores the block row by row with 16-B stores (two
-    // whole rows per instruction; a lane storing its own group would touch
-    // 64 cache lines per instruction).
+    // The stage buffers are free after the last barrier: each wave stages
+    // one 32-row block of its sub-tile at a time (32 x 128 fp32, row pitch
+    // 132 floats) and stores it row by row with 16-B stores.
+    // IRHT: before the store every lane takes two whole 32-column groups of
+    // the block and replaces each by H^-1((alpha acc) with masked entries
+    // zeroed), H^-1 y = s o (c FWHT(y)) (a lane storing its own group would
+    // touch 64 cache lines per instruction).  BF16: the store pass rounds
+    // eight consecutive values per lane to bf16.
     static_assert(WM * WN * 32 * 132 * 4 <= 2 * kStageLds, "epilogue staging exceeds LDS");
     static_assert(FN * 32 == 128 && kBN / WN == 128, "the store pass assumes 128-column wave sub-tiles");
     float* stg = reinterpret_cast<float*>(lds) + wave * (32 * 132);
     const int gpr = N / 32;  // mask words per row
-    const rsrc_t rM = make_rsrc(cmask + (size_t)m0 * gpr, (uint32_t)rowsC * (uint32_t)gpr * 4u);
+    const rsrc_t rM = make_rsrc(EPI == kEpiIrht ? cmask + (size_t)m0 * gpr : nullptr,
+                                EPI == kEpiIrht ? (uint32_t)rowsC * (uint32_t)gpr * 4u : 0u);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -405,57 +423,78 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
           stg[(8 * (v / 4) + 4 * fh + (v % 4)) * 132 + 32 * j + fr] = alpha * acc[i][j][v];
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
       __builtin_amdgcn_wave_barrier();
+      if constexpr (EPI == kEpiIrht) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int item = lane + 64 * u;             // 32 rows x 4 groups
-        const int rl = item >> 2, gq = item & 3;
-        float t[32];
+        for (int u = 0; u < 2; ++u) {
+          const int item = lane + 64 * u;             // 32 rows x 4 groups
+          const int rl = item >> 2, gq = item & 3;
+          float t[32];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 w = *reinterpret_cast<const float4*>(stg + rl * 132 + 32 * gq + 4 * q);
-          t[4 * q] = w.x; t[4 * q + 1] = w.y; t[4 * q + 2] = w.z; t[4 * q + 3] = w.w;
-        }
-        const int col0 = n0 + wn * (kBN / WN) + 32 * gq;     // first column of the group
-        const uint32_t badc = 0u - (uint32_t)(col0 >= N);
-        const int row = wm * (kBM / WM) + i * 32 + rl;       // within the tile
-        const uint32_t moff = ((((uint32_t)row * (uint32_t)gpr + (uint32_t)(col0 >> 5)) * 4u) & ~badc) | (kOOB & badc);
-        const uint32_t mb = buf_load4(rM, moff);
-#pragma unroll
-        for (int e = 0; e < 32; ++e) t[e] = ((mb >> e) & 1u) ? 0.0f : t[e];
-#pragma unroll
-        for (int h = 1; h < 32; h <<= 1)
-#pragma unroll
-          for (int e = 0; e < 32; ++e) {
-            if (e & h) continue;
-            const float a = t[e], b = t[e + h];
-            t[e] = a + b;
-            t[e + h] = a - b;
+          for (int q = 0; q < 8; ++q) {
+            const float4 w = *reinterpret_cast<const float4*>(stg + rl * 132 + 32 * gq + 4 * q);
+            t[4 * q] = w.x; t[4 * q + 1] = w.y; t[4 * q + 2] = w.z; t[4 * q + 3] = w.w;
           }
+          const int col0 = n0 + wn * (kBN / WN) + 32 * gq;     // first column of the group
+          const uint32_t badc = 0u - (uint32_t)(col0 >= N);
+          const int row = wm * (kBM / WM) + i * 32 + rl;       // within the tile
+          const uint32_t moff = ((((uint32_t)row * (uint32_t)gpr + (uint32_t)(col0 >> 5)) * 4u) & ~badc) | (kOOB & badc);
+          const uint32_t mb = buf_load4(rM, moff);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          float o[4];
+          for (int e = 0; e < 32; ++e) t[e] = ((mb >> e) & 1u) ? 0.0f : t[e];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k = 4 * q + e;
-            const float y = t[k] * 0x1.6a09e6p-3f;  // fl32(1/sqrt(32))
-            o[e] = __uint_as_float(__float_as_uint(y) ^ (((sign_mask >> k) & 1u) << 31));
+          for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+              if (e & h) continue;
+              const float a = t[e], b = t[e + h];
+              t[e] = a + b;
+              t[e + h] = a - b;
+            }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int k = 4 * q + e;
+              const float y = t[k] * 0x1.6a09e6p-3f;  // fl32(1/sqrt(32))
+              o[e] = __uint_as_float(__float_as_uint(y) ^ (((sign_mask >> k) & 1u) << 31));
+            }
+            *reinterpret_cast<float4*>(stg + rl * 132 + 32 * gq + 4 * q) = float4{o[0], o[1], o[2], o[3]};
           }
-          *reinterpret_cast<float4*>(stg + rl * 132 + 32 * gq + 4 * q) = float4{o[0], o[1], o[2], o[3]};
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // the transformed block is in LDS
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // the transformed block is in LDS
-      __builtin_amdgcn_wave_barrier();
-      // row-contiguous stores: one instruction covers two 128-column rows
+      if constexpr (EPI == kEpiIrht) {
+        // row-contiguous stores: one instruction covers two 128-column rows
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int f = 64 * k + lane, rl = f >> 5, c4 = f & 31;
-        const float4 w = *reinterpret_cast<const float4*>(stg + rl * 132 + 4 * c4);
-        const int row = wm * (kBM / WM) + i * 32 + rl;
-        const int col = n0 + wn * (kBN / WN) + 4 * c4;
-        const uint32_t bad = 0u - (uint32_t)(col >= N);
-        const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 4u) & ~bad) | (kOOB & bad);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, w), rC, (int)off, 0, kStoreNT);
+        for (int k = 0; k < 16; ++k) {
+          const int f = 64 * k + lane, rl = f >> 5, c4 = f & 31;
+          const float4 w = *reinterpret_cast<const float4*>(stg + rl * 132 + 4 * c4);
+          const int row = wm * (kBM / WM) + i * 32 + rl;
+          const int col = n0 + wn * (kBN / WN) + 4 * c4;
+          const uint32_t bad = 0u - (uint32_t)(col >= N);
+          const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 4u) & ~bad) | (kOOB & bad);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, w), rC, (int)off, 0, kStoreNT);
+        }
+      } else {
+        // bf16: eight consecutive columns per lane, one instruction covers
+        // four 128-column rows
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int f = 64 * k + lane, rl = f >> 4, c8 = f & 15;
+          const float4 w0 = *reinterpret_cast<const float4*>(stg + rl * 132 + 8 * c8);
+          const float4 w1 = *reinterpret_cast<const float4*>(stg + rl * 132 + 8 * c8 + 4);
+          const int row = wm * (kBM / WM) + i * 32 + rl;
+          const int col = n0 + wn * (kBN / WN) + 8 * c8;
+          const uint32_t bad = 0u - (uint32_t)(col >= N);
+          const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 2u) & ~bad) | (kOOB & bad);
+          const __attribute__((ext_vector_type(4))) unsigned int o = {
+              bf16_rne(w0.x) | (bf16_rne(w0.y) << 16), bf16_rne(w0.z) | (bf16_rne(w0.w) << 16),
+              bf16_rne(w1.x) | (bf16_rne(w1.y) << 16), bf16_rne(w1.z) | (bf16_rne(w1.w) << 16)};
+          __builtin_amdgcn_raw_buffer_store_b128(o, rC, (int)off, 0, kStoreNT);
+        }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // this block's reads are done before it is overwritten
       __builtin_amdgcn_wave_barrier();
@@ -463,23 +502,23 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
   }
 }
 
-template <int FMT, bool VEC, int WM, int WN, bool IRHT>
+template <int FMT, bool VEC, int WM, int WN, int EPI>
 hipError_t gemm_launch_cfg(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                            int64_t m, int64_t n, int64_t k, float alpha, const float* ga,
                            const float* gb, float* c, int64_t ldc, const uint32_t* cmask,
                            uint32_t sign_mask, hipStream_t s) {
   const size_t lds = 2 * (size_t)kStageLds;
-  const void* fn = reinterpret_cast<const void*>(&mx_gemm_kernel<FMT, VEC, WM, WN, IRHT>);
+  const void* fn = reinterpret_cast<const void*>(&mx_gemm_kernel<FMT, VEC, WM, WN, EPI>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
-  hipLaunchKernelGGL((mx_gemm_kernel<FMT, VEC, WM, WN, IRHT>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((mx_gemm_kernel<FMT, VEC, WM, WN, EPI>), dim3((unsigned)tiles),
                      dim3(Waves<WM, WN>::kThreads), lds, s, a, as, b, bs, (int)m, (int)n, (int)k,
                      alpha, ga, gb, c, (int)ldc, cmask, sign_mask);
   return hipGetLastError();
 }
 
-template <int FMT, bool IRHT>
+template <int FMT, int EPI>
 hipError_t gemm_launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                        int64_t m, int64_t n, int64_t k, float alpha, const float* ga,
                        const float* gb, float* c, int64_t ldc, const uint32_t* cmask,
@@ -487,9 +526,9 @@ hipError_t gemm_launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, co
   // scale rows split into whole per-stage words when K is a stage multiple
   const bool vec = (k / 32) % Fmt<FMT>::kGroups == 0;
   if (vec)
-    return gemm_launch_cfg<FMT, true, FP4MX_GEMM_WM, FP4MX_GEMM_WN, IRHT>(
+    return gemm_launch_cfg<FMT, true, FP4MX_GEMM_WM, FP4MX_GEMM_WN, EPI>(
         a, as, b, bs, m, n, k, alpha, ga, gb, c, ldc, cmask, sign_mask, s);
-  return gemm_launch_cfg<FMT, false, FP4MX_GEMM_WM, FP4MX_GEMM_WN, IRHT>(
+  return gemm_launch_cfg<FMT, false, FP4MX_GEMM_WM, FP4MX_GEMM_WN, EPI>(
       a, as, b, bs, m, n, k, alpha, ga, gb, c, ldc, cmask, sign_mask, s);
 }
 
@@ -498,21 +537,28 @@ hipError_t gemm_launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, co
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                           int64_t m, int64_t n, int64_t k, float alpha, float* c, int64_t ldc,
                           hipStream_t s) {
-  return gemm_launch<4, false>(a, as, b, bs, m, n, k, alpha, nullptr, nullptr, c, ldc, nullptr, 0u, s);
+  return gemm_launch<4, kEpiF32>(a, as, b, bs, m, n, k, alpha, nullptr, nullptr, c, ldc, nullptr, 0u, s);
 }
 
 hipError_t launch_mx_gemm_irht(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                                const uint8_t* bs, int64_t m, int64_t n, int64_t k, float alpha,
                                float* c, int64_t ldc, const uint8_t* cmask, uint32_t sign_mask,
                                hipStream_t s) {
-  return gemm_launch<4, true>(a, as, b, bs, m, n, k, alpha, nullptr, nullptr, c, ldc,
-                              reinterpret_cast<const uint32_t*>(cmask), sign_mask, s);
+  return gemm_launch<4, kEpiIrht>(a, as, b, bs, m, n, k, alpha, nullptr, nullptr, c, ldc,
+                                  reinterpret_cast<const uint32_t*>(cmask), sign_mask, s);
+}
+
+hipError_t launch_mx_gemm_bf16(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                               const uint8_t* bs, int64_t m, int64_t n, int64_t k, float alpha,
+                               uint16_t* c, int64_t ldc, hipStream_t s) {
+  return gemm_launch<4, kEpiBf16>(a, as, b, bs, m, n, k, alpha, nullptr, nullptr,
+                                  reinterpret_cast<float*>(c), ldc, nullptr, 0u, s);
 }
 
 hipError_t launch_fp8_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                            const float* ga, const float* gb, int64_t m, int64_t n, int64_t k,
                            float* c, int64_t ldc, hipStream_t s) {
-  return gemm_launch<0, false>(a, as, b, bs, m, n, k, 1.0f, ga, gb, c, ldc, nullptr, 0u, s);
+  return gemm_launch<0, kEpiF32>(a, as, b, bs, m, n, k, 1.0f, ga, gb, c, ldc, nullptr, 0u, s);
 }
 
 }  // namespace fp4mx

@@ -146,6 +146,20 @@ FP4MX_API int fp4mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const 
                const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, float alpha,
                float* c, int64_t ldc, void* stream);
 
+/* The same GEMM with a bf16 output: C[i][j] = bf16_RNE(fp32 result), i.e.
+ * exactly the value fp4mx_gemm writes, rounded to nearest even (NaN stays
+ * NaN).  C: bf16 bits [m][ldc], 16-B aligned, ldc >= n, ldc a multiple of 8.
+ * Arguments and errors otherwise as fp4mx_gemm.  Halves the output traffic
+ * for callers whose layer outputs are bf16 tensors.
+ * Source: the layer graphs of "Quartet II ..." -- "The Complete Quartet II
+ * Computation Graph" (linear-layer outputs and gradients flow as
+ * high-precision bf16 tensors between the FP4 GEMMs); the rounding step is
+ * this library's design. */
+FP4MX_API int fp4mx_gemm_bf16(const uint8_t* a_codes, const uint8_t* a_scales,
+                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t m,
+                              int64_t n, int64_t k, float alpha, uint16_t* c, int64_t ldc,
+                              void* stream);
+
 /* Saved forward context for the backward pass: the SR-quantized, RHT'd
  * transposed operands X^T [k][m] (groups along m) and W^T [k][n] (groups
  * along n), plus the seed.  All four buffers are caller-owned device memory:

@@ -88,6 +88,9 @@ def test_gemm_and_linear_validation():
     assert L.fp4mx_gemm(p, p, p, p, 64, 64, 0, 1.0, f, 64, None) == -2
     assert L.fp4mx_gemm(p, p, p, p, 64, 64, 64, 1.0, f, 60, None) == -2      # ldc < n
     assert L.fp4mx_gemm(None, p, p, p, 64, 64, 64, 1.0, f, 64, None) == -1
+    assert L.fp4mx_gemm_bf16(p, p, p, p, 64, 64, 64, 1.0, f, 68, None) == -3   # ldc not a multiple of 8
+    assert L.fp4mx_gemm_bf16(p, p, p, p, 64, 64, 64, 1.0, None, 64, None) == -1
+    assert L.fp4mx_gemm_bf16(p, p, p, p, 64, 96, 64, 1.0, f, 64, None) == -2   # ldc < n
     # workspace too small
     ctx = binding.CtxStruct(p.value, p.value, p.value, p.value, 3)
     assert L.fp4mx_linear_fwd(p, p, 64, 64, 64, 3, f, C.byref(ctx), p, 16, None) == -5

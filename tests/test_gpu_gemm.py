@@ -71,3 +71,47 @@ def test_gemm_extreme_scales():
     qb = (rs.integers(0, 256, (32, 64), dtype=np.uint8), rs.integers(100, 150, (32, 4)).astype(np.uint8))
     c = cpu(fq.gemm(_to_dev_mx(*qa), _to_dev_mx(*qb)))
     assert rel_fro(c, mx.gemm(*qa, *qb)) <= TOL
+
+
+def _bf16_rne_bits(f32):
+    """fp32 -> bf16 bits, round to nearest even (the input generators' rounding)."""
+    return synth.f32_to_bf16_bits(np.asarray(f32, dtype=np.float32))
+
+
+@pytest.mark.parametrize("m,n,k,ldc", [(256, 256, 256, 256), (352, 160, 96, 168), (96, 544, 320, 552),
+                                       (32, 32, 32, 40)])
+def test_gemm_bf16_output(m, n, k, ldc):
+    """The bf16-output GEMM writes exactly bf16_RNE of the fp32 GEMM's value, and
+    agrees with the oracle's fp64 product rounded to bf16 (up to the fp32
+    accumulation crossing a rounding boundary: rare, and then one bf16 ulp)."""
+    log("gemm bf16 out", m, n, k, ldc)
+    a, b = _operands(m, n, k, seed=4)
+    qa = mx.quantize(host_f32(a), rounding=mx.SR, sign_mask=5, seed=3, stream=1)
+    qb = mx.quantize(host_f32(b), rounding=mx.SR, sign_mask=5, seed=3, stream=2)
+    A, B = _to_dev_mx(*qa), _to_dev_mx(*qb)
+    c32 = fq.gemm(A, B, alpha=16 / 9)
+    c16 = torch.full((m, ldc), 3.0, dtype=torch.bfloat16, device="cuda")
+    fq.gemm_bf16(A, B, alpha=16 / 9, out=c16[:, :n])
+    torch.cuda.synchronize()
+    got = cpu(c16.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(got[:, :n], _bf16_rne_bits(cpu(c32)))
+    assert np.all(got[:, n:] == 0x4040)                   # padding (3.0) untouched
+    want = _bf16_rne_bits(mx.gemm(*qa, *qb, alpha=mx.ALPHA_BWD).astype(np.float32))
+    diff = np.abs(got[:, :n].astype(np.int32) - want.astype(np.int32))
+    assert diff.max() <= 1 and np.mean(diff > 0) < 1e-3
+
+
+def test_gemm_bf16_output_full_size():
+    """Quartet workload shape (8192 x 4096, K 4096), launch as the step uses it:
+    the bf16 output equals bf16_RNE of the fp32 GEMM bit for bit."""
+    m, n, k = 8192, 4096, 4096
+    log("gemm bf16 out full size", m, n, k)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    A = fq.MXTensor(torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device="cuda", generator=g),
+                    torch.randint(118, 130, (m, k // 32), dtype=torch.uint8, device="cuda", generator=g))
+    B = fq.MXTensor(torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device="cuda", generator=g),
+                    torch.randint(118, 130, (n, k // 32), dtype=torch.uint8, device="cuda", generator=g))
+    c32 = fq.gemm(A, B)
+    c16 = fq.gemm_bf16(A, B)
+    torch.cuda.synchronize()
+    assert np.array_equal(cpu(c16.view(torch.int16)).view(np.uint16), _bf16_rne_bits(cpu(c32)))
