@@ -42,7 +42,13 @@ int check_device() {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-bool dim_ok(int64_t d) { return d > 0 && d % 32 == 0; }
+// Largest dimension (and GEMM output leading dimension) accepted.  The GEMM
+// addresses each 256-row tile through a buffer resource whose range must stay
+// at or below the 2^31-byte out-of-range offset (256 rows x 2^21 fp32 =
+// 2^31 B; 256 rows x 2^21 x 1 B of FP8 codes), and the tile kernels' grid
+// y-extents (cols / 64 or / 128) stay far inside the launch limits.
+constexpr int64_t kMaxDim = FP4MX_MAX_DIM;
+bool dim_ok(int64_t d) { return d > 0 && d % 32 == 0 && d <= kMaxDim; }
 
 size_t round_up(size_t v) { return (v + 255) & ~(size_t)255; }
 size_t mx_bytes(int64_t rows, int64_t cols) {  // codes + scales, each padded
@@ -88,7 +94,7 @@ int quantize_impl(const void* x, int64_t rows, int64_t cols, int64_t ld, int axi
 int check_gemm_args(const void* a, const void* as, const void* b, const void* bs, int64_t m,
                     int64_t n, int64_t k, const float* c, int64_t ldc) {
   if (!a || !as || !b || !bs || !c) return FP4MX_E_NULL;
-  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k) || ldc < n) return FP4MX_E_SHAPE;
+  if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k) || ldc < n || ldc > kMaxDim) return FP4MX_E_SHAPE;
   if (!aligned16(a) || !aligned16(b) || !aligned16(c) || ldc % 4 != 0) return FP4MX_E_ALIGN;
   return FP4MX_OK;
 }
@@ -108,7 +114,7 @@ const char* fp4mx_status_string(int status) {
   switch (status) {
     case FP4MX_OK: return "ok";
     case FP4MX_E_NULL: return "null pointer";
-    case FP4MX_E_SHAPE: return "bad shape (dimensions must be positive multiples of 32)";
+    case FP4MX_E_SHAPE: return "bad shape (dimensions must be positive multiples of 32, at most 2^21)";
     case FP4MX_E_ALIGN: return "bad alignment (16-byte pointers, leading dimension multiple of 8)";
     case FP4MX_E_ARG: return "bad argument";
     case FP4MX_E_WORKSPACE: return "workspace missing or too small";

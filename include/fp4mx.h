@@ -15,7 +15,9 @@
  *   before any launch; on a validation error nothing is enqueued.  A HIP
  *   launch error returns FP4MX_E_HIP and fp4mx_last_hip_error() gives the HIP
  *   code (per calling thread).
- * - Shapes: every dimension must be a positive multiple of 32 (FP4MX_E_SHAPE).
+ * - Shapes: every dimension must be a positive multiple of 32 and at most
+ *   FP4MX_MAX_DIM = 2^21; a GEMM output's leading dimension ldc is at most
+ *   FP4MX_MAX_DIM too (FP4MX_E_SHAPE otherwise).
  *   Pointers must be 16-byte aligned and leading dimensions (in elements) a
  *   multiple of 8 (FP4MX_E_ALIGN).  The device must be gfx950 (FP4MX_E_DEVICE).
  * - bf16 inputs are row-major with leading dimension `ld` (elements).
@@ -72,10 +74,14 @@
 extern "C" {
 #endif
 
+/* Largest accepted dimension (rows, cols, m, n, k) and GEMM output ldc. */
+#define FP4MX_MAX_DIM 2097152
+
 typedef enum {
   FP4MX_OK = 0,
   FP4MX_E_NULL = -1,      /* a required pointer is NULL                       */
-  FP4MX_E_SHAPE = -2,     /* a dimension is <= 0 or not a multiple of 32      */
+  FP4MX_E_SHAPE = -2,     /* a dimension <= 0, not a multiple of 32, or above
+                             FP4MX_MAX_DIM                                    */
   FP4MX_E_ALIGN = -3,     /* pointer not 16-B aligned / ld not multiple of 8  */
   FP4MX_E_ARG = -4,       /* bad enum value or argument combination           */
   FP4MX_E_WORKSPACE = -5, /* workspace NULL or smaller than required          */

@@ -81,6 +81,24 @@ def test_quantize_validation(case):
     assert L.fp4mx_status_string(st)
 
 
+def test_maximum_dimension_rejected():
+    """Dimensions (and a GEMM's output ldc) above 2^21 are refused before any
+    launch: the GEMM's per-tile buffer ranges must stay within 2^31 bytes."""
+    L = binding.lib()
+    keep, p = _buf()
+    f = C.c_void_p(p.value)
+    big = (1 << 21) + 32
+    assert L.fp4mx_quantize(p, 64, big, big, 0, 0, 0, 0, p, p, None) == -2
+    assert L.fp4mx_quantize(p, big, 64, 64, 1, 0, 0, 0, p, p, None) == -2
+    assert L.fp4mx_gemm(p, p, p, p, 64, 64, big, 1.0, f, 64, None) == -2
+    assert L.fp4mx_gemm(p, p, p, p, big, 64, 64, 1.0, f, 64, None) == -2
+    assert L.fp4mx_gemm(p, p, p, p, 64, 64, 64, 1.0, f, big, None) == -2      # ldc above the maximum
+    assert L.fp4mx_gemm_bf16(p, p, p, p, 64, 64, 64, 1.0, f, big, None) == -2
+    assert L.fp4nv_linear_fwd(p, p, 64, 64, big, f, p, 1 << 20, None) == -2
+    assert L.fp4mx_linear_workspace_bytes(64, 64, big) == 0
+    assert b"2^21" in L.fp4mx_status_string(-2)
+
+
 def test_gemm_and_linear_validation():
     L = binding.lib()
     keep, p = _buf()
