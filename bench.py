@@ -313,6 +313,41 @@ def gemm_roofline(st, avg):
             "per_launch_ms": {x: round(avg[x], 4) for x in fl}}
 
 
+def mfma_sustained(iters=20000, reps=3):
+    """Sustained rate of the GEMM's FP4 scaled MFMA on this GPU, measured with
+    libfp4mx_probe.so (16 independent MFMAs per iteration per wave, one
+    workgroup of 4 waves per CU, no memory traffic in the loop), with random
+    operand bits and with all-zero operands, and the shader clock of the run
+    (shader-clock counter over the 100-MHz reference counter)."""
+    import ctypes
+    import torch
+    from fp4_microscaled_quantized_amd import build as fbuild
+    lib = ctypes.CDLL(fbuild.PROBE_LIB)
+    lib.fp4mx_probe_mfma_fp4.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    blocks = 256
+    stream = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device="cuda").manual_seed(7)
+    words = {"random_operands": torch.randint(-2 ** 31, 2 ** 31 - 1, (2048,), dtype=torch.int32, device="cuda",
+                                              generator=g),
+             "zero_operands": torch.zeros(2048, dtype=torch.int32, device="cuda")}
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(4, dtype=torch.int64, device="cuda")
+    flops = blocks * 4.0 * iters * 16 * 2 * 32 * 32 * 64
+    out = {"probe": "v_mfma_scale_f32_32x32x64_f8f6f4, FP4 x FP4, %d workgroups x 4 waves x %d x 16 MFMAs"
+                    % (blocks, iters)}
+    for kind, w in words.items():
+        def call(i):
+            st_ = lib.fp4mx_probe_mfma_fp4(w.data_ptr(), iters, blocks, sink.data_ptr(), clk.data_ptr(), stream)
+            if st_ != 0:
+                raise RuntimeError("MFMA probe launch failed: %d" % st_)
+        ms = _time_calls(call, reps, 1)
+        c = clk.cpu().numpy().astype(np.uint64)
+        ghz = float(c[1] - c[0]) / (float(c[3] - c[2]) / 100e6) / 1e9
+        out[kind] = {"TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "clock_GHz": round(ghz, 3)}
+    return out
+
+
 def quant_roofline(st, avg):
     m, n, k = st.m, st.n, st.k
     # dual quantizer: 2 B read + two outputs of 0.5 + 1/32 B per element
@@ -602,11 +637,15 @@ def main():
         "data": "synthetic", "config": {**wl, "seed": 0, "parallelism": "none (1 GPU)"},
         "frac_fp4_peak": round(value / PEAK_FP4_TFLOPS, 4),
         "roofline": gemm_roofline(st, avg),
+        "mfma_fp4_sustained": mfma_sustained(),
         "breakdown_ms": {k2: round(v, 4) for k2, v in avg.items()},
         "kernel_sum_ms_per_step": round(ev_ms, 4),
         "event_ms_per_step": round(float(np.mean(step_ms)), 4),
         "quantizer_roofline_in_step": quant_roofline(st, avg),
     }
+    sus = out["mfma_fp4_sustained"]["random_operands"]["TFLOP/s"]
+    out["roofline"]["sustained_peak_random_operands"] = sus
+    out["roofline"]["frac_of_sustained"] = round(out["roofline"]["achieved"] / sus, 4)
     del st
     torch.cuda.empty_cache()
     if not a.no_extra:
