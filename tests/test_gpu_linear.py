@@ -122,3 +122,30 @@ def test_quartet_workload_full_size():
 
 def test_llama_ffn_up_workload_full_size():
     _sampled_full_size(synth.llama_ffn_up(0), seed=0)
+
+
+def test_autograd_function():
+    """FP4LinearFunction under torch.autograd: Y and both gradients are the bf16
+    roundings (nearest even) of fp4mx_linear_fwd / _bwd's fp32 outputs, bit for
+    bit, and the fp32 values agree with the oracle's forward and backward."""
+    m, n, k, seed = 128, 96, 160, 6
+    xb = synth.normal_with_outliers((m, k), 4, 0)
+    wb = synth.normal((n, k), 0.02, 4, 1)
+    gb = synth.normal((m, n), 1e-3, 4, 2)
+    x = dev_bf16(xb).requires_grad_(True)
+    w = dev_bf16(wb).requires_grad_(True)
+    g = dev_bf16(gb)
+    y = fq.FP4LinearFunction.apply(x, w, seed)
+    y.backward(g)
+    y32, ctx = fq.linear_fwd(x.detach(), w.detach(), seed=seed)
+    dx32, dw32 = fq.linear_bwd(g, ctx)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.bfloat16 and x.grad.dtype == torch.bfloat16
+    bits = lambda t: cpu(t.detach().view(torch.int16)).view(np.uint16)
+    assert np.array_equal(bits(y), synth.f32_to_bf16_bits(cpu(y32)))
+    assert np.array_equal(bits(x.grad), synth.f32_to_bf16_bits(cpu(dx32)))
+    assert np.array_equal(bits(w.grad), synth.f32_to_bf16_bits(cpu(dw32)))
+    want_y, octx = mx.linear_fwd(host_f32(xb), host_f32(wb), seed)
+    want_dx, want_dw = mx.linear_bwd(host_f32(gb), octx)
+    assert rel_fro(cpu(y32), want_y) <= TOL
+    assert rel_fro(cpu(dx32), want_dx) <= TOL and rel_fro(cpu(dw32), want_dw) <= TOL
