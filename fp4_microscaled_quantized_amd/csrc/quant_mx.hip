@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fp4mx_internal.h"
 #include "mx_device.h"
 
@@ -39,15 +41,16 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kWaveStage = 64 * 64 + 16 * 4;  // 64 groups of 64 B, 16-B pad per 16 groups
 
+// Groups of workgroup-block `blk` (4 waves x 64 groups); `ws` is this wave's
+// LDS stage.
 template <bool HAD, int ROUND>
-__global__ __launch_bounds__(256) void quant_row_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
-    uint32_t key_lo, uint32_t key_hi, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, FastDiv gdiv, uint32_t ngroups) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[4 * kWaveStage];
+__device__ __forceinline__ void row_block(uint32_t blk, uint8_t* ws, const uint16_t* __restrict__ x,
+                                          int64_t cols, int64_t ld, uint32_t sign_mask,
+                                          uint32_t key_lo, uint32_t key_hi,
+                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                          FastDiv gdiv, uint32_t ngroups) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint8_t* ws = stage + wave * kWaveStage;
-  const uint32_t g_wave = blockIdx.x * 256u + (uint32_t)wave * 64u;  // first group of the wave
+  const uint32_t g_wave = blk * 256u + (uint32_t)wave * 64u;  // first group of the wave
   if (g_wave >= ngroups) return;
   // cooperative coalesced load: chunk q*64 + lane (16 B) of the wave's 64 groups
 #pragma unroll
@@ -90,6 +93,30 @@ __global__ __launch_bounds__(256) void quant_row_kernel(
   u32x4 o = {w[0], w[1], w[2], w[3]};
   *reinterpret_cast<u32x4*>(codes + row * (cols / 2) + grp * 16) = o;
   scales[row * gpr + grp] = (uint8_t)sc;
+}
+
+// RTN is bandwidth-bound: a grid of about one residency (8 workgroups per CU)
+// strides over the blocks, so no partial last wave of workgroups idles the
+// memory system (8192 x 4096: 18.5 instead of 22 us).  SR is ALU-bound and
+// runs one block per workgroup (the loop costs it registers and 10%).
+template <bool HAD, int ROUND>
+__global__ __launch_bounds__(256) void quant_row_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
+    uint32_t key_lo, uint32_t key_hi, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, FastDiv gdiv, uint32_t ngroups, uint32_t nblk) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4 * kWaveStage];
+  uint8_t* ws = stage + (threadIdx.x >> 6) * kWaveStage;
+  if constexpr (ROUND == FP4MX_ROUND_RTN) {
+    for (uint32_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+      row_block<HAD, ROUND>(blk, ws, x, cols, ld, sign_mask, key_lo, key_hi, codes, scales, gdiv,
+                            ngroups);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // this block's LDS reads are done before the next writes
+    }
+  } else {
+    row_block<HAD, ROUND>(blockIdx.x, ws, x, cols, ld, sign_mask, key_lo, key_hi, codes, scales,
+                          gdiv, ngroups);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -201,6 +228,20 @@ hipError_t tile_dispatch(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
   return hipErrorInvalidValue;
 }
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 }  // namespace
 
 hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
@@ -208,22 +249,24 @@ hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64
   const int64_t groups = rows * (cols / kGroup);
   if (groups >= (1ll << 31)) return launch_quant_tile(x, rows, cols, ld, hadamard, &o, nullptr, s);
   const FastDiv gd = make_fastdiv((uint32_t)(cols / kGroup));
-  const unsigned nblk = (unsigned)((groups + 255) / 256);
+  const uint32_t nblk = (uint32_t)((groups + 255) / 256);
   const uint32_t ng = (uint32_t)groups;
+  const uint32_t resident = (uint32_t)cu_count() * 8u;
+  const unsigned grid = o.rounding == FP4MX_ROUND_RTN && nblk > resident ? resident : nblk;
   if (hadamard) {
     if (o.rounding == FP4MX_ROUND_RTN)
-      hipLaunchKernelGGL((quant_row_kernel<true, 0>), dim3(nblk), dim3(256), 0, s, x, rows, cols,
-                         ld, o.sign_mask, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng);
+      hipLaunchKernelGGL((quant_row_kernel<true, 0>), dim3(grid), dim3(256), 0, s, x, rows, cols,
+                         ld, o.sign_mask, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng, nblk);
     else
-      hipLaunchKernelGGL((quant_row_kernel<true, 1>), dim3(nblk), dim3(256), 0, s, x, rows, cols,
-                         ld, o.sign_mask, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng);
+      hipLaunchKernelGGL((quant_row_kernel<true, 1>), dim3(grid), dim3(256), 0, s, x, rows, cols,
+                         ld, o.sign_mask, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng, nblk);
   } else {
     if (o.rounding == FP4MX_ROUND_RTN)
-      hipLaunchKernelGGL((quant_row_kernel<false, 0>), dim3(nblk), dim3(256), 0, s, x, rows, cols,
-                         ld, 0u, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng);
+      hipLaunchKernelGGL((quant_row_kernel<false, 0>), dim3(grid), dim3(256), 0, s, x, rows, cols,
+                         ld, 0u, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng, nblk);
     else
-      hipLaunchKernelGGL((quant_row_kernel<false, 1>), dim3(nblk), dim3(256), 0, s, x, rows, cols,
-                         ld, 0u, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng);
+      hipLaunchKernelGGL((quant_row_kernel<false, 1>), dim3(grid), dim3(256), 0, s, x, rows, cols,
+                         ld, 0u, o.key.lo, o.key.hi, o.codes, o.scales, gd, ng, nblk);
   }
   return hipGetLastError();
 }
