@@ -1,7 +1,8 @@
 // Per-group device arithmetic shared by the MXFP4 kernels (quant_mx.hip,
 // quest.hip): the in-register block-32 FWHT, bf16 unpacking and sign flips,
 // the counter hash of the SR draws, and the MX group quantizer (E8M0 scale
-// from the group maximum; RTN by the hardware converter, SR in integers).
+// from the group maximum; RTN by the hardware converter, SR by exact fp32
+// comparisons of the draw with the position between grid points).
 //
 // Sources: "Quartet: Native FP4 Training Can Be Optimal for Large Language
 // Models" -- "The Hadamard Transform: Why It Is Necessary and How It Is

@@ -15,13 +15,15 @@
 //  - One lane owns one 32-element group: the whole FWHT (5 butterfly stages)
 //    runs in registers with no cross-lane traffic, the group maximum is a
 //    register reduction, and the lane writes its 16 code bytes with one 16-B
-//    store.  Row-axis groups are read straight from HBM with 16-B loads.
+//    store.  Row-axis groups are staged per wave through LDS so the global
+//    reads are coalesced 16-B loads.
 //  - Column-axis groups (the transposed operand) go through a 128 x 64 bf16
 //    LDS tile: one coalesced read of the tile feeds both the row-axis and the
 //    column-axis quantizer, so the dual kernel reads each input byte once.
 //  - RTN uses gfx950's v_cvt_scalef32_pk_fp4_f32, which computes E2M1
 //    round-to-nearest-even of x / scale with saturation (two elements per
-//    instruction, the sign included); SR is done in integer/fp32 arithmetic.
+//    instruction, the sign included); SR uses exact fp32 comparisons and a
+//    counter hash per element.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
