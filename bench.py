@@ -615,7 +615,7 @@ def cpu_baseline(rows=1024, target_s=15.0):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1",
+        print("bench.py measures one GPU only (the library has no multi-GPU path); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     import torch
