@@ -89,3 +89,24 @@ def test_quantizer_workload_full_size_row(rounding):
 def test_quantizer_workload_full_size_col_sr():
     bits = synth.quantizer_tensor()["x"]
     _check(bits, fq.COL, fq.SR, True, mask=rng.sign_mask(0, 0), seed=0, stream=1, what="c2-full-col")
+
+
+def test_col_axis_scales_at_odd_address():
+    """Column-axis output whose scale pointer is not 4-byte aligned (scales
+    are bytes; only codes must be 16-B aligned): same bytes as the oracle."""
+    from fp4_microscaled_quantized_amd.binding import _check, _ptr, _stream
+    R, C = 256, 192
+    bits = synth.normal_with_outliers((R, C), seed=3, tensor_id=0)
+    x = dev_bf16(bits)
+    codes = torch.empty((C, R // 2), dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((C * (R // 32) + 8,), 0xAB, dtype=torch.uint8, device="cuda")
+    m = rng.sign_mask(3, 2)
+    log("col axis, scales at offset 1")
+    _check(fq.lib().fp4mx_hadamard_quantize(_ptr(x), R, C, C, fq.COL, fq.SR, m, 4, 3, _ptr(codes),
+                                            sbuf.data_ptr() + 1, _stream()))
+    torch.cuda.synchronize()
+    wc, ws = mx.quantize(host_f32(bits), rounding=mx.SR, axis=mx.COL, sign_mask=m, seed=4, stream=3)
+    got = cpu(sbuf)
+    assert_bytes_equal(cpu(codes), wc, "codes")
+    assert_bytes_equal(got[1:1 + ws.size].reshape(ws.shape), ws, "scales")
+    assert got[0] == 0xAB and np.all(got[1 + ws.size:] == 0xAB)
