@@ -179,6 +179,7 @@ __global__ __launch_bounds__(256) void quest_row_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kTileR = 128, kTileC = 64;
 constexpr int kPitch = kTileC * 2 + 16;
+constexpr int kCoutPitch = (kTileR / kGroup) * 16 + 16;  // output staging: 64 B + pad per column
 
 // bf16 bits of E2M1 code q (sign in bit 3) times X = 2^(e-127), exact.
 __device__ __forceinline__ uint32_t deq_bf16(uint32_t q, float X) {
@@ -221,6 +222,11 @@ __global__ __launch_bounds__(256) void requant_tile_kernel(
     }
   }
   __syncthreads();
+  // output codes and scales are staged per tile and stored as whole row
+  // pieces (64 code bytes and one scale word per output row), as in the
+  // column-axis quantizer
+  __shared__ __attribute__((aligned(16))) uint8_t cout[kTileC * kCoutPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t cscl[kTileC * (kTileR / kGroup)];
   const int c = tid & 63, rg = tid >> 6;
   if (c < nc && rg * kGroup < nr) {
     float t[kGroup];
@@ -235,8 +241,20 @@ __global__ __launch_bounds__(256) void requant_tile_kernel(
     uint32_t w[4], sc;
     quant_group<ROUND>(t, (uint32_t)idx0, group_kmix(idx0, klo, khi), w, sc);
     u32x4 o = {w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<u32x4*>(out_codes + orow * (rows / 2) + grp * 16) = o;
-    out_scales[orow * (rows / kGroup) + grp] = (uint8_t)sc;
+    *reinterpret_cast<u32x4*>(cout + c * kCoutPitch + rg * 16) = o;
+    cscl[c * (kTileR / kGroup) + rg] = (uint8_t)sc;
+  }
+  __syncthreads();
+  const int oc = tid >> 2, q = tid & 3;  // output row c0 + oc, its q-th group of this tile
+  if (oc < nc && q * kGroup < nr) {
+    *reinterpret_cast<u32x4*>(out_codes + (c0 + oc) * (rows / 2) + (r0 / kGroup + q) * 16) =
+        *reinterpret_cast<const u32x4*>(cout + oc * kCoutPitch + q * 16);
+    uint8_t* sp = out_scales + (c0 + oc) * (rows / kGroup) + r0 / kGroup;
+    if (nr == kTileR && (rows / kGroup) % 4 == 0 && ((uintptr_t)out_scales & 3u) == 0) {
+      if (q == 0) *reinterpret_cast<uint32_t*>(sp) = *reinterpret_cast<const uint32_t*>(cscl + oc * 4);
+    } else {
+      sp[q] = cscl[oc * (kTileR / kGroup) + q];
+    }
   }
 }
 
