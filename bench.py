@@ -313,32 +313,37 @@ def gemm_roofline(st, avg):
             "per_launch_ms": {x: round(avg[x], 4) for x in fl}}
 
 
-def mfma_sustained(iters=20000, reps=3):
-    """Sustained rate of the GEMM's FP4 scaled MFMA on this GPU, measured with
-    libfp4mx_probe.so (16 independent MFMAs per iteration per wave, one
-    workgroup of 4 waves per CU, no memory traffic in the loop), with random
-    operand bits and with all-zero operands, and the shader clock of the run
-    (shader-clock counter over the 100-MHz reference counter)."""
+def mfma_sustained(fmt=4, iters=20000, reps=3):
+    """Sustained rate of the GEMMs' scaled MFMA (fmt 4: FP4 x FP4, 0: FP8 E4M3
+    x FP8) on this GPU, measured with libfp4mx_probe.so (16 independent MFMAs
+    per iteration per wave, one workgroup of 4 waves per CU, no memory traffic
+    in the loop), with random operand bits and with all-zero operands, and the
+    shader clock of the run (shader-clock counter over the 100-MHz reference
+    counter)."""
     import ctypes
     import torch
     from fp4_microscaled_quantized_amd import build as fbuild
     lib = ctypes.CDLL(fbuild.PROBE_LIB)
-    lib.fp4mx_probe_mfma_fp4.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.fp4mx_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     blocks = 256
     stream = torch.cuda.current_stream().cuda_stream
     g = torch.Generator(device="cuda").manual_seed(7)
-    words = {"random_operands": torch.randint(-2 ** 31, 2 ** 31 - 1, (2048,), dtype=torch.int32, device="cuda",
-                                              generator=g),
-             "zero_operands": torch.zeros(2048, dtype=torch.int32, device="cuda")}
+    rnd = torch.randint(-2 ** 31, 2 ** 31 - 1, (4096,), dtype=torch.int32, device="cuda", generator=g)
+    if fmt == 0:
+        # E4M3 bytes with the NaN encodings (0x7f, 0xff) replaced by the largest finite value
+        b = rnd.view(torch.uint8).clone()
+        b[(b & 0x7f) == 0x7f] -= 1
+        rnd = b.view(torch.int32)
+    words = {"random_operands": rnd, "zero_operands": torch.zeros(4096, dtype=torch.int32, device="cuda")}
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     clk = torch.zeros(4, dtype=torch.int64, device="cuda")
     flops = blocks * 4.0 * iters * 16 * 2 * 32 * 32 * 64
-    out = {"probe": "v_mfma_scale_f32_32x32x64_f8f6f4, FP4 x FP4, %d workgroups x 4 waves x %d x 16 MFMAs"
-                    % (blocks, iters)}
+    out = {"probe": "v_mfma_scale_f32_32x32x64_f8f6f4, %s, %d workgroups x 4 waves x %d x 16 MFMAs"
+                    % ("FP4 x FP4" if fmt == 4 else "FP8 E4M3 x E4M3", blocks, iters)}
     for kind, w in words.items():
         def call(i):
-            st_ = lib.fp4mx_probe_mfma_fp4(w.data_ptr(), iters, blocks, sink.data_ptr(), clk.data_ptr(), stream)
+            st_ = lib.fp4mx_probe_mfma(fmt, w.data_ptr(), iters, blocks, sink.data_ptr(), clk.data_ptr(), stream)
             if st_ != 0:
                 raise RuntimeError("MFMA probe launch failed: %d" % st_)
         ms = _time_calls(call, reps, 1)
@@ -649,7 +654,7 @@ def main():
         "data": "synthetic", "config": {**wl, "seed": 0, "parallelism": "none (1 GPU)"},
         "frac_fp4_peak": round(value / PEAK_FP4_TFLOPS, 4),
         "roofline": gemm_roofline(st, avg),
-        "mfma_fp4_sustained": mfma_sustained(),
+        "mfma_fp4_sustained": mfma_sustained(4),
         "breakdown_ms": {k2: round(v, 4) for k2, v in avg.items()},
         "kernel_sum_ms_per_step": round(ev_ms, 4),
         "event_ms_per_step": round(float(np.mean(step_ms)), 4),
@@ -675,6 +680,9 @@ def main():
         out["quantizer"] = time_quantizer(max(a.steps, 20), a.warmup)
         torch.cuda.empty_cache()
         out["nvfp4"] = time_nvfp4(max(a.steps // 2, 5), 2)
+        out["nvfp4"]["mfma_fp8_sustained"] = mfma_sustained(0)
+        sus8 = out["nvfp4"]["mfma_fp8_sustained"]["random_operands"]["TFLOP/s"]
+        out["nvfp4"]["frac_fp8_sustained"] = round(out["nvfp4"]["TFLOP/s"] / sus8, 4)
         torch.cuda.empty_cache()
         out["nvfp4_bwd_ms_eden"] = time_nvfp4_bwd(max(a.steps // 2, 5), 2)
         torch.cuda.empty_cache()
