@@ -98,6 +98,38 @@ def e2m1_sr(v: np.ndarray, u: np.ndarray) -> np.ndarray:
     return code | _sign_bit(v)
 
 
+def e2m1_sr_carry(v: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """Stochastic rounding onto the E2M1 grid driven by 32 random bits ``r``
+    per element: the MXFP4 quantizer's backward rounding.
+
+    The pages fix the rounding probability ("Quartet: Native FP4 Training
+    ...", the SR step of the backward quantization; "NVFP4 Format and
+    Standard Stochastic Rounding", Step 3): for a <= |v| < b with a, b
+    adjacent grid points the magnitude becomes b with probability
+    p = (|v|-a)/(b-a).  How the random bits realise that is this library's
+    choice: the draw is u = (r >> 1) * 2^-31, the top 31 bits of r, and b is
+    taken iff u >= 1 - p.  Equivalently, (r >> 1) + floor(p * 2^31) carries
+    past 2^31: a 31-bit uniform added to the gap fraction, then truncated.
+    P(b) = p exactly whenever p * 2^31 is an integer, which holds for every
+    fp32 |v| >= 2^-9; below that the probability is at most 2^-31 under p.
+    The sign is the sign of v (a negative value that rounds to 0 gives -0).
+    Requires |v| <= 6 (the callers' scales guarantee no clipping).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v.astype(np.float64))
+    if np.any(a > 6.0):
+        raise ValueError("e2m1_sr_carry needs |v| <= 6")
+    lo = np.minimum(np.searchsorted(E2M1_GRID, a, side="right") - 1, 7)   # grid[lo] <= a
+    hi = np.minimum(lo + 1, 7)
+    gap = np.where(hi > lo, E2M1_GRID[hi] - E2M1_GRID[lo], 1.0)
+    p = np.where(hi > lo, (a - E2M1_GRID[lo]) / gap, 0.0)       # exact in float64
+    t = np.floor(p * 2.0 ** 31).astype(np.uint64)               # exact: p < 1
+    u31 = (np.asarray(r, dtype=np.uint32) >> np.uint32(1)).astype(np.uint64)
+    up = (u31 + t) >= np.uint64(1 << 31)
+    code = np.where(up, hi, lo).astype(np.uint8)
+    return code | _sign_bit(v)
+
+
 def e8m0_code(amax: np.ndarray) -> np.ndarray:
     """Shared MXFP4 scale exponent for a group with maximum magnitude ``amax``.
 

@@ -45,7 +45,9 @@ def quantize(x: np.ndarray, *, rounding: int, axis: int = ROW, hadamard: bool = 
              output codes [C, R/2] (the transposed operand, K-major).
     rounding RTN (forward): v = fl(y * 2^(127-e)), E2M1 round-to-nearest-even,
              saturating.  SR (backward): v = fl(y * (3/4 * 2^(127-e))) and
-             stochastic rounding; |v| < 6 always holds, so nothing clips.
+             stochastic rounding (``formats.e2m1_sr_carry``: up iff
+             (r >> 1) * 2^-31 >= 1 - p); |v| < 6 always holds, so nothing
+             clips.
     hadamard apply the block-32 RHT with ``sign_mask`` first.
 
     The scale byte e comes from the group maximum of y (before the 3/4), see
@@ -82,9 +84,9 @@ def quantize(x: np.ndarray, *, rounding: int, axis: int = ROW, hadamard: bool = 
         rid = np.arange(R, dtype=np.uint64) if row_ids is None else np.asarray(row_ids, dtype=np.uint64)
         idx = (rid[:, None] * np.uint64(C)
                + np.arange(C, dtype=np.uint64)[None, :]).reshape(R, C // 32, 32)
-        u = rng.uniform24(rng.bits(seed, stream, idx))
+        r = rng.bits(seed, stream, idx)
         v = np.where(finite[:, :, None], v, 0).astype(np.float32)
-        q = formats.e2m1_sr(v, u)
+        q = formats.e2m1_sr_carry(v, r)
     else:
         raise ValueError("rounding must be RTN or SR")
     q = np.where(finite[:, :, None], q, 0).astype(np.uint8)

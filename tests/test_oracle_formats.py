@@ -1,5 +1,7 @@
 """Pins for the oracle's codecs (E2M1, E8M0, E4M3) against the pages and
 independent routes (numpy's round-half-even, torch's float8_e4m3fn)."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -73,6 +75,55 @@ def test_e2m1_sr_unbiased_monte_carlo():
     n = 20000
     u = rs.random((n, 64))
     q = formats.e2m1_decode(formats.e2m1_sr(np.broadcast_to(v, (n, 64)), u))
+    mean = q.mean(axis=0)
+    sd = q.std(axis=0) / np.sqrt(n) + 1e-12
+    assert np.all(np.abs(mean - v) < 5 * sd + 1e-9)
+
+
+def _sr_bits_below_gap(vf):
+    """Number of fraction bits of |v|'s position inside its E2M1 gap (fp32 v)."""
+    a = abs(float(vf))
+    if a >= 1.0:
+        return 22                      # 24-bit significand, gap 2^(e-1)
+    e = math.frexp(a)[1] - 1           # a in [2^e, 2^(e+1))
+    return 22 - e                      # gap 0.5 against ulp 2^(e-23)
+
+
+def test_e2m1_sr_carry_exact_over_a_complete_stratum():
+    # With D = the bits of |v| below the gap, the decision depends on the top D
+    # bits of r >> 1 only; enumerating all 2^D of them, exactly p * 2^D round up,
+    # so the mean of the decoded values is |v| to the last bit.
+    for v in [1.3, 2.7, 5.1, 4.0, 5.999999, 0.7, 0.3, 0.26, 1.0000001, 0.5, 6.0]:
+        vf = np.float32(v)
+        d = _sr_bits_below_gap(vf)
+        k = np.arange(1 << d, dtype=np.uint64)
+        r = (k << np.uint64(32 - d)).astype(np.uint32) | np.uint32(1)   # the dropped bit is ignored
+        dec = formats.e2m1_decode(formats.e2m1_sr_carry(np.full(k.shape, vf), r))
+        assert dec.sum() / float(1 << d) == float(vf), v
+
+
+def test_e2m1_sr_carry_orientation_and_sign():
+    # the largest draw rounds every interior point up, the smallest none
+    v = np.array([0.1, 0.75, 1.2, 2.5, 4.5, -0.1, -3.5, 1e-30, -0.0, 0.0], dtype=np.float32)
+    hi = formats.e2m1_decode(formats.e2m1_sr_carry(v, np.full(v.shape, 0xFFFFFFFF, np.uint32)))
+    lo = formats.e2m1_decode(formats.e2m1_sr_carry(v, np.zeros(v.shape, np.uint32)))
+    assert list(hi) == [0.5, 1.0, 1.5, 3.0, 6.0, -0.5, -4.0, 0.0, 0.0, 0.0]
+    assert list(lo) == [0.0, 0.5, 1.0, 2.0, 4.0, -0.0, -3.0, 0.0, 0.0, 0.0]
+    # sign bit follows v, also for values that round to zero and for -0
+    q = formats.e2m1_sr_carry(v, np.zeros(v.shape, np.uint32))
+    assert list(q >> 3) == [0, 0, 0, 0, 0, 1, 1, 0, 1, 0]
+    # p * 2^31 is an integer for |v| >= 2^-9 ... and for smaller |v| the
+    # probability falls short of p by less than 2^-31: v = 2^-40 never rounds up
+    assert formats.e2m1_sr_carry(np.float32(2.0 ** -40), np.uint32(0xFFFFFFFF)) == 0
+    assert formats.e2m1_sr_carry(np.float32(2.0 ** -32), np.uint32(0xFFFFFFFF)) == 1
+
+
+def test_e2m1_sr_carry_unbiased_monte_carlo():
+    rs = np.random.default_rng(6)
+    v = (rs.random(64) * 12 - 6).astype(np.float32)
+    n = 20000
+    r = rs.integers(0, 1 << 32, (n, 64), dtype=np.uint64).astype(np.uint32)
+    q = formats.e2m1_decode(formats.e2m1_sr_carry(np.broadcast_to(v, (n, 64)), r))
     mean = q.mean(axis=0)
     sd = q.std(axis=0) / np.sqrt(n) + 1e-12
     assert np.all(np.abs(mean - v) < 5 * sd + 1e-9)

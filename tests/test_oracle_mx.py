@@ -1,5 +1,6 @@
 """Pins for the oracle's MXFP4 quantizer, GEMM and linear layer."""
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -13,7 +14,7 @@ def _bf16ish(rs, shape, scale=1.0):
     return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits((rs.standard_normal(shape) * scale).astype(np.float32)))
 
 
-def _brute_block_rtn(x_block, mask, hadamard, rounding, u=None):
+def _brute_block_rtn(x_block, mask, hadamard, rounding, r=None):
     """Pure-Python restatement for one 32-block (integer-valued inputs make the
     transform exact, so a plain matrix product stands in for the FWHT)."""
     H = scipy.linalg.hadamard(32)
@@ -42,8 +43,9 @@ def _brute_block_rtn(x_block, mask, hadamard, rounding, u=None):
             if lo == 7:
                 bc = 7
             else:
-                p = (abs(v) - grid[lo]) / (grid[lo + 1] - grid[lo])
-                bc = lo + 1 if u[i] < p else lo
+                # exact rational position in the gap, against the 31-bit draw
+                p = (Fraction(abs(v)) - Fraction(grid[lo])) / Fraction(grid[lo + 1] - grid[lo])
+                bc = lo + 1 if Fraction(int(r[i]) >> 1, 2 ** 31) >= 1 - p else lo
         # a transformed value that is exactly zero may carry either sign (the
         # fp32 butterflies keep IEEE signed zeros); mark it with None
         out.append(None if yi == 0 else bc | (8 if math.copysign(1.0, v) < 0 else 0))
@@ -64,8 +66,8 @@ def test_quantize_vs_pure_python(rounding, hadamard):
     for r in range(3):
         for b in range(2):
             idx = np.arange(r * 64 + b * 32, r * 64 + b * 32 + 32, dtype=np.uint64)
-            u = rng.uniform24(rng.bits(seed, stream, idx))
-            want, e = _brute_block_rtn(x[r, b * 32:(b + 1) * 32], mask, hadamard, rounding, u)
+            rb = rng.bits(seed, stream, idx)
+            want, e = _brute_block_rtn(x[r, b * 32:(b + 1) * 32], mask, hadamard, rounding, rb)
             assert scales[r, b] == e
             got = list(q[r, b * 32:(b + 1) * 32])
             assert [g if w is not None else (g & 7) for g, w in zip(got, want)] == \
