@@ -107,11 +107,12 @@ def e2m1_sr_carry(v: np.ndarray, r: np.ndarray) -> np.ndarray:
     Standard Stochastic Rounding", Step 3): for a <= |v| < b with a, b
     adjacent grid points the magnitude becomes b with probability
     p = (|v|-a)/(b-a).  How the random bits realise that is this library's
-    choice: the draw is u = (r >> 1) * 2^-31, the top 31 bits of r, and b is
-    taken iff u >= 1 - p.  Equivalently, (r >> 1) + floor(p * 2^31) carries
-    past 2^31: a 31-bit uniform added to the gap fraction, then truncated.
-    P(b) = p exactly whenever p * 2^31 is an integer, which holds for every
-    fp32 |v| >= 2^-9; below that the probability is at most 2^-31 under p.
+    choice, at 22 bits, the fraction bits an fp32 significand keeps below an
+    E2M1 gap of a normal value: the draw is u = (r >> 10) * 2^-22, and b is
+    taken iff floor(p * 2^22) + (r >> 10) >= 2^22, i.e. the gap fraction
+    truncated to 22 bits plus a 22-bit uniform carries.  P(b) =
+    floor(p * 2^22) / 2^22: exactly p for every fp32 |v| >= 1, and for
+    smaller |v| less than 2^-22 below p (a bias under 2^-23 of the scale).
     The sign is the sign of v (a negative value that rounds to 0 gives -0).
     Requires |v| <= 6 (the callers' scales guarantee no clipping).
     """
@@ -123,9 +124,9 @@ def e2m1_sr_carry(v: np.ndarray, r: np.ndarray) -> np.ndarray:
     hi = np.minimum(lo + 1, 7)
     gap = np.where(hi > lo, E2M1_GRID[hi] - E2M1_GRID[lo], 1.0)
     p = np.where(hi > lo, (a - E2M1_GRID[lo]) / gap, 0.0)       # exact in float64
-    t = np.floor(p * 2.0 ** 31).astype(np.uint64)               # exact: p < 1
-    u31 = (np.asarray(r, dtype=np.uint32) >> np.uint32(1)).astype(np.uint64)
-    up = (u31 + t) >= np.uint64(1 << 31)
+    t = np.floor(p * 2.0 ** 22).astype(np.uint64)               # exact: p < 1
+    u22 = (np.asarray(r, dtype=np.uint32) >> np.uint32(10)).astype(np.uint64)
+    up = (u22 + t) >= np.uint64(1 << 22)
     code = np.where(up, hi, lo).astype(np.uint8)
     return code | _sign_bit(v)
 

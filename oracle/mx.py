@@ -46,8 +46,8 @@ def quantize(x: np.ndarray, *, rounding: int, axis: int = ROW, hadamard: bool = 
     rounding RTN (forward): v = fl(y * 2^(127-e)), E2M1 round-to-nearest-even,
              saturating.  SR (backward): v = fl(y * (3/4 * 2^(127-e))) and
              stochastic rounding (``formats.e2m1_sr_carry``: up iff
-             (r >> 1) * 2^-31 >= 1 - p); |v| < 6 always holds, so nothing
-             clips.
+             floor(p * 2^22) + (r >> 10) >= 2^22); |v| < 6 always holds,
+             so nothing clips.
     hadamard apply the block-32 RHT with ``sign_mask`` first.
 
     The scale byte e comes from the group maximum of y (before the 3/4), see

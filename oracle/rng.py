@@ -17,7 +17,7 @@ from two published mixing functions,
 Per (seed, stream): key = splitmix64(seed XOR (stream << 32)).
 Per element with output-operand linear index i = row * cols + col:
     r(i) = fmix32(lo32(i) ^ lo32(key) ^ fmix32(hi32(i) ^ hi32(key))).
-The MXFP4 quantizer's SR draw is u = (r >> 1) * 2^-31 (formats.e2m1_sr_carry);
+The MXFP4 quantizer's SR draw is u = (r >> 10) * 2^-22 (formats.e2m1_sr_carry);
 the NVFP4 SR baseline and MS-EDEN draw u = (r >> 8) * 2^-24.
 RHT sign mask of GEMM g: lo32(splitmix64(seed XOR ((0x5100 + g) << 32))).
 """

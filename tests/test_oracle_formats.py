@@ -80,26 +80,23 @@ def test_e2m1_sr_unbiased_monte_carlo():
     assert np.all(np.abs(mean - v) < 5 * sd + 1e-9)
 
 
-def _sr_bits_below_gap(vf):
-    """Number of fraction bits of |v|'s position inside its E2M1 gap (fp32 v)."""
-    a = abs(float(vf))
-    if a >= 1.0:
-        return 22                      # 24-bit significand, gap 2^(e-1)
-    e = math.frexp(a)[1] - 1           # a in [2^e, 2^(e+1))
-    return 22 - e                      # gap 0.5 against ulp 2^(e-23)
-
-
 def test_e2m1_sr_carry_exact_over_a_complete_stratum():
-    # With D = the bits of |v| below the gap, the decision depends on the top D
-    # bits of r >> 1 only; enumerating all 2^D of them, exactly p * 2^D round up,
-    # so the mean of the decoded values is |v| to the last bit.
-    for v in [1.3, 2.7, 5.1, 4.0, 5.999999, 0.7, 0.3, 0.26, 1.0000001, 0.5, 6.0]:
+    # The decision depends on the top 22 bits of r only.  Enumerating all 2^22
+    # of them, the fraction that rounds up is p truncated to 22 bits: exactly
+    # p for |v| >= 1 and for smaller |v| whose gap position has <= 22 bits, so
+    # the decoded mean is |v| to the last bit there ...
+    k = np.arange(1 << 22, dtype=np.uint64)
+    r = ((k << np.uint64(10)) | np.uint64(0x2A5)).astype(np.uint32)   # the low 10 bits are ignored
+    for v in [1.3, 2.7, 5.1, 4.0, 5.999999, 1.0000001, 6.0, -3.3, 0.625, 0.2578125, 0.5]:
         vf = np.float32(v)
-        d = _sr_bits_below_gap(vf)
-        k = np.arange(1 << d, dtype=np.uint64)
-        r = (k << np.uint64(32 - d)).astype(np.uint32) | np.uint32(1)   # the dropped bit is ignored
         dec = formats.e2m1_decode(formats.e2m1_sr_carry(np.full(k.shape, vf), r))
-        assert dec.sum() / float(1 << d) == float(vf), v
+        assert dec.sum() / float(1 << 22) == float(vf), v
+    # ... and below 1 the mean falls short of |v| by less than 2^-22 of the gap
+    for v in [0.7, 0.3, 0.26, 0.1, 1e-3, 3e-7]:
+        vf = np.float32(v)
+        dec = formats.e2m1_decode(formats.e2m1_sr_carry(np.full(k.shape, vf), r))
+        short = float(vf) - dec.sum() / float(1 << 22)
+        assert 0.0 <= short < 0.5 * 2.0 ** -22, (v, short)
 
 
 def test_e2m1_sr_carry_orientation_and_sign():
@@ -112,10 +109,10 @@ def test_e2m1_sr_carry_orientation_and_sign():
     # sign bit follows v, also for values that round to zero and for -0
     q = formats.e2m1_sr_carry(v, np.zeros(v.shape, np.uint32))
     assert list(q >> 3) == [0, 0, 0, 0, 0, 1, 1, 0, 1, 0]
-    # p * 2^31 is an integer for |v| >= 2^-9 ... and for smaller |v| the
-    # probability falls short of p by less than 2^-31: v = 2^-40 never rounds up
-    assert formats.e2m1_sr_carry(np.float32(2.0 ** -40), np.uint32(0xFFFFFFFF)) == 0
-    assert formats.e2m1_sr_carry(np.float32(2.0 ** -32), np.uint32(0xFFFFFFFF)) == 1
+    # a gap position below 2^-22 never rounds up; 2^-22 itself does with the largest draw
+    assert formats.e2m1_sr_carry(np.float32(2.0 ** -24), np.uint32(0xFFFFFFFF)) == 0
+    assert formats.e2m1_sr_carry(np.float32(2.0 ** -23), np.uint32(0xFFFFFFFF)) == 1
+    assert formats.e2m1_sr_carry(np.float32(2.0 ** -23), np.uint32(0xFFFFFBFF)) == 0
 
 
 def test_e2m1_sr_carry_unbiased_monte_carlo():

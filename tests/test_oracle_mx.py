@@ -43,9 +43,11 @@ def _brute_block_rtn(x_block, mask, hadamard, rounding, r=None):
             if lo == 7:
                 bc = 7
             else:
-                # exact rational position in the gap, against the 31-bit draw
+                # exact rational position in the gap, cut to 22 bits, against
+                # the 22-bit draw
                 p = (Fraction(abs(v)) - Fraction(grid[lo])) / Fraction(grid[lo + 1] - grid[lo])
-                bc = lo + 1 if Fraction(int(r[i]) >> 1, 2 ** 31) >= 1 - p else lo
+                p22 = Fraction(math.floor(p * 2 ** 22), 2 ** 22)
+                bc = lo + 1 if Fraction(int(r[i]) >> 10, 2 ** 22) >= 1 - p22 else lo
         # a transformed value that is exactly zero may carry either sign (the
         # fp32 butterflies keep IEEE signed zeros); mark it with None
         out.append(None if yi == 0 else bc | (8 if math.copysign(1.0, v) < 0 else 0))
