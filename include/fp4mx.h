@@ -46,8 +46,11 @@
  *   - 2, 0), i.e. 2^(e-127) = 2^(floor(log2 max|y|) - 2).
  *   RTN: E2M1 round-to-nearest-even of y * 2^(127-e), saturating at 6.
  *   SR:  v = fl32(y * (0.75 * 2^(127-e))) (|v| < 6 always); with a <= |v| < b
- *        adjacent grid points, take b iff (r >> 8) * 2^-24 < (|v|-a)/(b-a),
- *        where r = fmix32(lo32(i) ^ lo32(k) ^ fmix32(hi32(i) ^ hi32(k))),
+ *        adjacent grid points and p = (|v|-a)/(b-a), take b iff
+ *        floor(p * 2^22) + (r >> 10) >= 2^22 (P(b) = p for |v| >= 1, within
+ *        2^-22 below it under 1); the sign is v's, so a negative value that
+ *        rounds to 0 gives -0.  Here
+ *        r = fmix32(lo32(i) ^ lo32(k) ^ fmix32(hi32(i) ^ hi32(k))),
  *        k = splitmix64(seed ^ (rng_stream << 32)) and i = row * cols_out + col
  *        is the element's index in the OUTPUT operand.
  *   Sources: "Quartet: Native FP4 Training ..." -- "The Hadamard Transform:
