@@ -117,14 +117,15 @@ def gemm_exact(a_codes, a_scales, a_g, b_codes, b_scales, b_g) -> np.ndarray:
     return dequantize(a_codes, a_scales, a_g) @ dequantize(b_codes, b_scales, b_g).T
 
 
-def fp8_stage(codes, scales):
+def fp8_stage_bytes(codes, scales):
     """The FP8 staging of an NVFP4 operand used by the library's GEMM.
 
     Per 32-element K block (two 16-groups with scales s_lo, s_hi):
     e_blk = max(floor(log2 s_lo), floor(log2 s_hi)) - 5 over the non-zero
     scales (0 if both are zero); each element becomes
     E4M3_RNE(q * s16 * 2^-e_blk) and the block carries the power of two
-    2^e_blk.  Returns (fp8 values as float64 [R, C], e_blk int [R, C/32]).
+    2^e_blk.  Returns (E4M3 bytes uint8 [R, C], e_blk int [R, C/32]); a
+    negative code of magnitude 0 stages as -0 (0x80).
     This staging is this library's design (the pages run NVFP4 natively);
     with the -5 offset the largest staged magnitude is 6 * 1.875 * 2^5 = 360.
     """
@@ -137,8 +138,14 @@ def fp8_stage(codes, scales):
     emax = ex.max(axis=2)
     e_blk = np.where(np.isfinite(emax), emax - 5, 0).astype(np.int64)
     prod = q * np.repeat(s, 16, axis=1) * np.ldexp(1.0, -np.repeat(e_blk, 32, axis=1))
-    staged = formats.e4m3_decode(formats.e4m3_rne(prod))
-    return staged, e_blk
+    return formats.e4m3_rne(prod), e_blk
+
+
+def fp8_stage(codes, scales):
+    """``fp8_stage_bytes`` decoded: (staged values as float64 [R, C], e_blk)."""
+    b, e_blk = fp8_stage_bytes(codes, scales)
+    return formats.e4m3_decode(b), e_blk
+
 
 
 def gemm_fp8_staged(a_codes, a_scales, a_g, b_codes, b_scales, b_g) -> np.ndarray:

@@ -98,3 +98,75 @@ def test_nvfp4_workload_full_size_sampled():
     err = rel_fro(y[np.ix_(ri, cj)], nvfp4.gemm_fp8_staged(*qx, *qw))
     log("  sampled rel err %.2e" % err)
     assert err <= TOL
+
+
+def _random_nv_operand(rows, cols, seed, zero_blocks=True):
+    """Random E2M1 code bytes and positive E4M3 scale bytes (normal and
+    subnormal, some zero; with zero_blocks, some 32-blocks with both scales 0)."""
+    rs = np.random.default_rng(seed)
+    codes = rs.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = rs.integers(0, 0x7F, (rows, cols // 16), dtype=np.uint8)     # 0x7F is NaN
+    scales[rs.random(scales.shape) < 0.05] = 0
+    scales[rs.random(scales.shape) < 0.1] &= 0x07                          # subnormal scales
+    if zero_blocks:
+        zb = rs.random((rows, cols // 32)) < 0.03
+        scales.reshape(rows, cols // 32, 2)[zb] = 0
+    return codes, scales
+
+
+def _staged_from_workspace(m, n, k, a, b, row_sample=None):
+    """Run fp4nv_gemm through the C ABI and read the FP8-staged operands back
+    from its workspace (A's E4M3 [m, k] and E8M0 [m, k/32], then B's, each
+    piece 256-B aligned)."""
+    from fp4_microscaled_quantized_amd.binding import _check, _ptr, _stream
+    L = fq.lib()
+    ru = lambda v: (v + 255) // 256 * 256
+    ws = torch.empty(L.fp4nv_gemm_workspace_bytes(m, n, k), dtype=torch.uint8, device="cuda")
+    dev = lambda t: torch.from_numpy(np.ascontiguousarray(t)).cuda()
+    ac, asc, bc, bsc = dev(a[0]), dev(a[1]), dev(b[0]), dev(b[1])
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    _check(L.fp4nv_gemm(_ptr(ac), _ptr(asc), _ptr(one), _ptr(bc), _ptr(bsc), _ptr(one), m, n, k,
+                        _ptr(c), n, _ptr(ws), ws.numel(), _stream()))
+    torch.cuda.synchronize()
+    o = 0
+    fa = ws[o:o + m * k].view(m, k); o += ru(m * k)
+    ea = ws[o:o + m * k // 32].view(m, k // 32); o += ru(m * k // 32)
+    fb = ws[o:o + n * k].view(n, k); o += ru(n * k)
+    eb = ws[o:o + n * k // 32].view(n, k // 32)
+    if row_sample is not None:
+        ra, rb = row_sample
+        return cpu(fa[ra]), cpu(ea[ra]), cpu(fb[rb]), cpu(eb[rb])
+    return cpu(fa), cpu(ea), cpu(fb), cpu(eb)
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 32, 128), (96, 160, 320), (256, 64, 1024), (32, 32, 32)])
+def test_fp8_staging_bytes_exact(m, n, k):
+    """The staged E4M3 bytes and E8M0 block scales equal the oracle's staging
+    bit for bit (byte work), including zero and subnormal E4M3 scales, blocks
+    whose two scales are both 0, and negative zero codes."""
+    log("fp8 staging", m, n, k)
+    a, b = _random_nv_operand(m, k, 21), _random_nv_operand(n, k, 22)
+    fa, ea, fb, eb = _staged_from_workspace(m, n, k, a, b)
+    for what, got_f, got_e, op in (("A", fa, ea, a), ("B", fb, eb, b)):
+        want_f, want_e = nvfp4.fp8_stage_bytes(*op)
+        assert_bytes_equal(got_f, want_f, what + " staged E4M3")
+        assert_bytes_equal(got_e, (want_e + 127).astype(np.uint8), what + " E8M0 block scales")
+
+
+def test_fp8_staging_bytes_full_size_sampled():
+    """NVFP4 workload shape (M=16384, N=K=8192) in the forward's launch
+    configuration; staging is row-independent, so sampled rows of both staged
+    operands are compared with the oracle bit for bit."""
+    m, n, k = 16384, 8192, 8192
+    log("fp8 staging full size", m, n, k)
+    a, b = _random_nv_operand(m, k, 23), _random_nv_operand(n, k, 24)
+    rs = np.random.default_rng(25)
+    ra = np.sort(np.concatenate([[0, m - 1], rs.choice(m, 30, replace=False)]))
+    rb = np.sort(np.concatenate([[0, n - 1], rs.choice(n, 30, replace=False)]))
+    fa, ea, fb, eb = _staged_from_workspace(m, n, k, a, b, (torch.from_numpy(ra).cuda(),
+                                                             torch.from_numpy(rb).cuda()))
+    for what, got_f, got_e, op, rows in (("A", fa, ea, a, ra), ("B", fb, eb, b, rb)):
+        want_f, want_e = nvfp4.fp8_stage_bytes(op[0][rows], op[1][rows])
+        assert_bytes_equal(got_f, want_f, what + " staged E4M3 (sampled rows)")
+        assert_bytes_equal(got_e, (want_e + 127).astype(np.uint8), what + " E8M0 (sampled rows)")
