@@ -181,12 +181,18 @@ constexpr int kTileR = 128, kTileC = 64;
 constexpr int kPitch = kTileC * 2 + 16;
 constexpr int kCoutPitch = (kTileR / kGroup) * 16 + 16;  // output staging: 64 B + pad per column
 
-// bf16 bits of E2M1 code q (sign in bit 3) times X = 2^(e-127), exact.
-__device__ __forceinline__ uint32_t deq_bf16(uint32_t q, float X) {
-  const uint32_t e = (q >> 1) & 3u, mm = q & 1u;
-  const float mag = e == 0 ? 0.5f * (float)mm : __uint_as_float(((e + 126u) << 23) | (mm << 22));
-  const uint32_t b = __float_as_uint(mag * X) | ((q & 8u) << 28);
-  return b >> 16;
+// The two E2M1 codes of byte B of w, each times X = 2^(e-127), as a bf16
+// pair word (low element in the low half).  gfx950's decode converter at
+// scale 1.0 gives the exact signed grid values; the products with X are exact
+// in fp32 and in bf16 (two significant bits), so the bf16 bits are the upper
+// halves, taken with one byte permute.  A 0xFF scale (X = NaN) makes both
+// values NaN, and the group then quantizes as a non-finite group.
+template <int B>
+__device__ __forceinline__ void deq_pair_bf16(uint32_t w, float X, uint32_t& out) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+  const float a = v.x * X, b = v.y * X;
+  out = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
 template <int ROUND>
@@ -212,10 +218,10 @@ __global__ __launch_bounds__(256) void requant_tile_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          o[j] = deq_bf16((cw[k] >> (8 * j)) & 0xFu, X) |
-                 (deq_bf16((cw[k] >> (8 * j + 4)) & 0xFu, X) << 16);
+        deq_pair_bf16<0>(cw[k], X, o[0]);
+        deq_pair_bf16<1>(cw[k], X, o[1]);
+        deq_pair_bf16<2>(cw[k], X, o[2]);
+        deq_pair_bf16<3>(cw[k], X, o[3]);
         const u32x4 ov = {o[0], o[1], o[2], o[3]};
         *reinterpret_cast<u32x4*>(tile + r * kPitch + h * 64 + k * 16) = ov;
       }
