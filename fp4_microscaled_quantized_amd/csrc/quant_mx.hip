@@ -99,8 +99,9 @@ __device__ __forceinline__ void row_block(uint32_t blk, uint8_t* ws, const uint1
 
 // RTN is bandwidth-bound: a grid of about one residency (8 workgroups per CU)
 // strides over the blocks, so no partial last wave of workgroups idles the
-// memory system (8192 x 4096: 18.5 instead of 22 us).  SR is ALU-bound and
-// runs one block per workgroup (the loop costs it registers and 10%).
+// memory system (8192 x 4096: 18.5 instead of 22 us).  SR runs one block per
+// workgroup: with the loop it took 6-14% longer (8192 x 4096: 30.2 against
+// 28.5 us).
 template <bool HAD, int ROUND>
 __global__ __launch_bounds__(256) void quant_row_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
