@@ -60,6 +60,9 @@ _SIGS = {
     "fp4mx_ctx_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4mx_linear_fwd": (_INT, [_P, _P, _I64, _I64, _I64, _U64, _P, C.POINTER(CtxStruct), _P, _SZ, _P]),
     "fp4mx_linear_bwd": (_INT, [_P, C.POINTER(CtxStruct), _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "fp4mx_linear_fwd_bf16": (_INT, [_P, _P, _I64, _I64, _I64, _U64, _P, C.POINTER(CtxStruct), _P, _SZ,
+                                     _P]),
+    "fp4mx_linear_bwd_bf16": (_INT, [_P, C.POINTER(CtxStruct), _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "fp4mx_quest_quantize": (_INT, [_P, _I64, _I64, _I64, C.c_float, _U32, _P, _P, _P, _P]),
     "fp4mx_requantize": (_INT, [_P, _P, _I64, _I64, _INT, _U32, _U64, _U32, _P, _P, _P]),
     "fp4mx_unmask_inverse_hadamard": (_INT, [_P, _I64, _I64, _I64, _P, _U32, _P]),
@@ -222,38 +225,53 @@ def workspace(m, n, k, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def linear_fwd(x, w, seed=0, want_ctx=True, ws=None, out=None):
-    """Y = X W^T (fp32) and, when asked, the backward context."""
+def _out_entry(dtype, f32_name, bf16_name):
+    if dtype == torch.float32:
+        return getattr(lib(), f32_name)
+    if dtype == torch.bfloat16:
+        return getattr(lib(), bf16_name)
+    raise ValueError("output dtype must be float32 or bfloat16")
+
+
+def linear_fwd(x, w, seed=0, want_ctx=True, ws=None, out=None, dtype=torch.float32):
+    """Y = X W^T (fp32, or bf16 with dtype=torch.bfloat16) and, when asked,
+    the backward context."""
     m, k, _ = _bf16_2d(x)
     n, k2, _ = _bf16_2d(w)
     if k2 != k or not x.is_contiguous() or not w.is_contiguous():
         raise ValueError("x [m,k], w [n,k] contiguous")
+    fn = _out_entry(dtype, "fp4mx_linear_fwd", "fp4mx_linear_fwd_bf16")
     dev = x.device
     ws = ws if ws is not None else workspace(m, n, k, dev)
-    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    y = out if out is not None else torch.empty((m, n), dtype=dtype, device=dev)
+    if y.dtype != dtype or not y.is_contiguous() or tuple(y.shape) != (m, n):
+        raise ValueError("out must be a contiguous [m, n] tensor of the output dtype")
     ctx = None
     cs = None
     if want_ctx:
         ctx = LinearCtx(_alloc_mx(k, m, dev), _alloc_mx(k, n, dev), seed)
         cs = C.byref(ctx.as_struct())
-    _check(lib().fp4mx_linear_fwd(_ptr(x), _ptr(w), m, n, k, seed, _ptr(y), cs, _ptr(ws),
-                                  ws.numel(), _stream(dev)))
+    _check(fn(_ptr(x), _ptr(w), m, n, k, seed, _ptr(y), cs, _ptr(ws), ws.numel(), _stream(dev)))
     return y, ctx
 
 
-def linear_bwd(dy, ctx: LinearCtx, ws=None, dx=None, dw=None):
-    """dX = 16/9 Q(dY) Q(W^T)^T, dW = 16/9 Q(dY^T) Q(X^T)^T (fp32)."""
+def linear_bwd(dy, ctx: LinearCtx, ws=None, dx=None, dw=None, dtype=torch.float32):
+    """dX = 16/9 Q(dY) Q(W^T)^T, dW = 16/9 Q(dY^T) Q(X^T)^T (fp32, or bf16
+    with dtype=torch.bfloat16)."""
     m, n, _ = _bf16_2d(dy)
     k = ctx.xt.codes.shape[0]
     if not dy.is_contiguous():
         raise ValueError("dy must be contiguous")
+    fn = _out_entry(dtype, "fp4mx_linear_bwd", "fp4mx_linear_bwd_bf16")
     dev = dy.device
     ws = ws if ws is not None else workspace(m, n, k, dev)
-    dx = dx if dx is not None else torch.empty((m, k), dtype=torch.float32, device=dev)
-    dw = dw if dw is not None else torch.empty((n, k), dtype=torch.float32, device=dev)
+    dx = dx if dx is not None else torch.empty((m, k), dtype=dtype, device=dev)
+    dw = dw if dw is not None else torch.empty((n, k), dtype=dtype, device=dev)
+    for t, shp in ((dx, (m, k)), (dw, (n, k))):
+        if t.dtype != dtype or not t.is_contiguous() or tuple(t.shape) != shp:
+            raise ValueError("dx [m, k] and dw [n, k] must be contiguous tensors of the output dtype")
     st = ctx.as_struct()
-    _check(lib().fp4mx_linear_bwd(_ptr(dy), C.byref(st), m, n, k, _ptr(dx), _ptr(dw), _ptr(ws),
-                                  ws.numel(), _stream(dev)))
+    _check(fn(_ptr(dy), C.byref(st), m, n, k, _ptr(dx), _ptr(dw), _ptr(ws), ws.numel(), _stream(dev)))
     return dx, dw
 
 
@@ -509,16 +527,23 @@ def nv_linear_bwd_ctx(dy, ctx: NvCtx, ws=None, dx=None, dw=None):
 # --------------------------- autograd wrapper --------------------------------
 
 class FP4LinearFunction(torch.autograd.Function):
-    """Y = X W^T with all three GEMMs in MXFP4 (fp32 outputs cast to X's dtype)."""
+    """Y = X W^T with all three GEMMs in MXFP4, for bf16 X and W.
+
+    Y, dX and dW come out of the library as bf16 (the GEMMs' bf16 epilogue:
+    round to nearest even of the fp32 result), so no cast runs outside it."""
 
     @staticmethod
     def forward(ctx, x, w, seed):
-        y, c = linear_fwd(x.contiguous(), w.contiguous(), seed=int(seed), want_ctx=True)
+        if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+            raise TypeError("FP4LinearFunction takes bf16 x and w")
+        y, c = linear_fwd(x.contiguous(), w.contiguous(), seed=int(seed), want_ctx=True,
+                          dtype=torch.bfloat16)
         ctx.fp4 = c
-        ctx.dtypes = (x.dtype, w.dtype)
-        return y.to(x.dtype)
+        return y
 
     @staticmethod
     def backward(ctx, gy):
-        dx, dw = linear_bwd(gy.to(torch.bfloat16).contiguous(), ctx.fp4)
-        return dx.to(ctx.dtypes[0]), dw.to(ctx.dtypes[1]), None
+        if gy.dtype != torch.bfloat16:
+            raise TypeError("FP4LinearFunction expects a bf16 output gradient")
+        dx, dw = linear_bwd(gy.contiguous(), ctx.fp4, dtype=torch.bfloat16)
+        return dx, dw, None

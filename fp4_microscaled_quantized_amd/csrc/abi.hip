@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -23,9 +24,20 @@ int hip_fail(hipError_t e) {
 }
 
 constexpr int kMaxDevices = 64;
+// Per-device cache of the architecture check, written once per device.
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
+// FP4MX_DEVICE_ARCH, when set to a name other than gfx950, stands in for the
+// queried architecture: every compute call refuses with FP4MX_E_DEVICE before
+// touching a device.  It lets a host without a GPU exercise the refusal path;
+// set to gfx950 (or unset) it changes nothing, the real query decides.
+bool arch_override_refuses() {
+  const char* a = getenv("FP4MX_DEVICE_ARCH");
+  return a && *a && strncmp(a, "gfx950", 6) != 0;
+}
+
 int check_device() {
+  if (arch_override_refuses()) return FP4MX_E_DEVICE;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
@@ -198,8 +210,20 @@ size_t fp4mx_ctx_bytes(int64_t m, int64_t n, int64_t k) {
   return (size_t)k * m / 2 + (size_t)k * m / 32 + (size_t)k * n / 2 + (size_t)k * n / 32;
 }
 
-int fp4mx_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t k, uint64_t seed,
-                     float* y, const fp4mx_ctx* ctx, void* ws, size_t ws_bytes, void* stream) {
+// Output element type of the linear entry points.
+enum class Out { F32, BF16 };
+
+static hipError_t gemm_out(Out o, const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                           const uint8_t* bs, int64_t m, int64_t n, int64_t k, float alpha, void* c,
+                           int64_t ldc, hipStream_t s) {
+  return o == Out::F32
+             ? launch_mx_gemm(a, as, b, bs, m, n, k, alpha, static_cast<float*>(c), ldc, s)
+             : launch_mx_gemm_bf16(a, as, b, bs, m, n, k, alpha, static_cast<uint16_t*>(c), ldc, s);
+}
+
+static int linear_fwd_impl(const void* x, const void* w, int64_t m, int64_t n, int64_t k,
+                           uint64_t seed, void* y, Out yo, const fp4mx_ctx* ctx, void* ws,
+                           size_t ws_bytes, void* stream) {
   if (!x || !w || !y) return FP4MX_E_NULL;
   if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return FP4MX_E_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return FP4MX_E_ALIGN;
@@ -232,12 +256,12 @@ int fp4mx_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t
     e = launch_quant_row(static_cast<const uint16_t*>(x), m, k, k, true, xr, s);
     if (e == hipSuccess) e = launch_quant_row(static_cast<const uint16_t*>(w), n, k, k, true, wr, s);
   }
-  if (e == hipSuccess) e = launch_mx_gemm(xq, xs, wq, wsc, m, n, k, 1.0f, y, n, s);
+  if (e == hipSuccess) e = gemm_out(yo, xq, xs, wq, wsc, m, n, k, 1.0f, y, n, s);
   return e == hipSuccess ? FP4MX_OK : hip_fail(e);
 }
 
-int fp4mx_linear_bwd(const void* dy, const fp4mx_ctx* ctx, int64_t m, int64_t n, int64_t k,
-                     float* dx, float* dw, void* ws, size_t ws_bytes, void* stream) {
+static int linear_bwd_impl(const void* dy, const fp4mx_ctx* ctx, int64_t m, int64_t n, int64_t k,
+                           void* dx, void* dw, Out go, void* ws, size_t ws_bytes, void* stream) {
   if (!dy || !ctx || !dx || !dw) return FP4MX_E_NULL;
   if (!ctx->xt_codes || !ctx->xt_scales || !ctx->wt_codes || !ctx->wt_scales) return FP4MX_E_NULL;
   if (!dim_ok(m) || !dim_ok(n) || !dim_ok(k)) return FP4MX_E_SHAPE;
@@ -259,9 +283,30 @@ int fp4mx_linear_bwd(const void* dy, const fp4mx_ctx* ctx, int64_t m, int64_t n,
   QuantOut c{FP4MX_ROUND_SR, fp4mx_sign_mask(seed, 2), make_key(seed, 3), tq, ts};
   const float alpha = 16.0f / 9.0f;
   hipError_t e = launch_quant_tile(static_cast<const uint16_t*>(dy), m, n, n, true, &r, &c, s);
-  if (e == hipSuccess) e = launch_mx_gemm(dq, ds, ctx->wt_codes, ctx->wt_scales, m, k, n, alpha, dx, k, s);
-  if (e == hipSuccess) e = launch_mx_gemm(tq, ts, ctx->xt_codes, ctx->xt_scales, n, k, m, alpha, dw, k, s);
+  if (e == hipSuccess) e = gemm_out(go, dq, ds, ctx->wt_codes, ctx->wt_scales, m, k, n, alpha, dx, k, s);
+  if (e == hipSuccess) e = gemm_out(go, tq, ts, ctx->xt_codes, ctx->xt_scales, n, k, m, alpha, dw, k, s);
   return e == hipSuccess ? FP4MX_OK : hip_fail(e);
+}
+
+int fp4mx_linear_fwd(const void* x, const void* w, int64_t m, int64_t n, int64_t k, uint64_t seed,
+                     float* y, const fp4mx_ctx* ctx, void* ws, size_t ws_bytes, void* stream) {
+  return linear_fwd_impl(x, w, m, n, k, seed, y, Out::F32, ctx, ws, ws_bytes, stream);
+}
+
+int fp4mx_linear_fwd_bf16(const void* x, const void* w, int64_t m, int64_t n, int64_t k,
+                          uint64_t seed, uint16_t* y, const fp4mx_ctx* ctx, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return linear_fwd_impl(x, w, m, n, k, seed, y, Out::BF16, ctx, ws, ws_bytes, stream);
+}
+
+int fp4mx_linear_bwd(const void* dy, const fp4mx_ctx* ctx, int64_t m, int64_t n, int64_t k,
+                     float* dx, float* dw, void* ws, size_t ws_bytes, void* stream) {
+  return linear_bwd_impl(dy, ctx, m, n, k, dx, dw, Out::F32, ws, ws_bytes, stream);
+}
+
+int fp4mx_linear_bwd_bf16(const void* dy, const fp4mx_ctx* ctx, int64_t m, int64_t n, int64_t k,
+                          uint16_t* dx, uint16_t* dw, void* ws, size_t ws_bytes, void* stream) {
+  return linear_bwd_impl(dy, ctx, m, n, k, dx, dw, Out::BF16, ws, ws_bytes, stream);
 }
 
 // ------------------------------- QuEST -------------------------------------

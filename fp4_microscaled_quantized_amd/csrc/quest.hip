@@ -9,7 +9,7 @@
 //    is a constant passed in by the caller), clamp to [-c sigma, c sigma],
 //    RTN, a clipping mask bit per element;
 //  - "The GPU Kernel Implementation" Stage 1: the E8M0 scale encodes the
-//    value the clip factor determines; mask bit set iff |x| > c sigma;
+//    value the clip factor determines; mask bit set for clipped elements;
 //  - the inverse Hadamard and clipping-mask correction:
 //    dx = 16/9 H^-1(dx_q with the clipped entries zeroed);
 //  - "The Complete Quartet Algorithm": the backward dequantizes the saved
@@ -19,8 +19,11 @@
 // Per group (fp32 throughout, the same steps as the oracle):
 //   E = floor(log2 max|y|) (0 for a zero group); z = y 2^-E;
 //   mu = tree(z)/32; var = tree((z - mu)^2)/32; sigma_z = sqrt(var);
-//   T_z = c sigma_z; code = max(floor(log2 T_z) + E + 125, 0) (0 if T_z = 0);
-//   T = T_z 2^E; clipped = |y| > T -> sign(y) T; E2M1 RNE of clamped / 2^(code-127).
+//   T_z = c sigma_z; code = min(max(floor(log2 T_z) + E + 125, 0), 254) (0 if
+//   T_z = 0); T = T_z 2^E; |y| > T -> sign(y) T; E2M1 RNE of clamped / X with
+//   X = 2^(code-127); mask bit = |y| > min(T, 6 X): the power-of-two scale
+//   puts the grid's end 6 X anywhere in [0.75 T, 1.5 T), and elements beyond
+//   it are clipped by the saturating rounding.
 // tree = adjacent pairs summed level by level in index order.
 //
 // Design (MI355X):
@@ -93,20 +96,26 @@ __device__ __forceinline__ void quest_group(const float (&y)[kGroup], float clip
   const float var = tree32(z) * 0.03125f;
   const float sig = __builtin_sqrtf(var);
   const float tz = clip * sig;
+  // E8M0 byte of T, at most 254 (an infinite T_z, i.e. clip * sigma beyond
+  // the fp32 range, encodes as 254 too: floor_log2_bits(inf) = 128)
   int code = 0;
-  if (tz > 0.0f) code = max(floor_log2_bits(__float_as_uint(tz)) + E + 125, 0);
+  if (tz > 0.0f) code = min(max(floor_log2_bits(__float_as_uint(tz)) + E + 125, 0), 254);
   const float T = __builtin_ldexpf(tz, E);
   scale = (uint32_t)code;
   // the converter computes E2M1 RNE (saturating) of v / X, X = 2^(code-127);
   // code 0 passes the subnormal 2^-127
   const float X = __uint_as_float(code == 0 ? 0x00400000u : (uint32_t)code << 23);
+  // the grid ends at 6 X (exact; +inf for code >= 253, where no finite
+  // element reaches it): elements beyond min(T, 6 X) are clipped, by the
+  // clamp or by the saturating rounding, and masked
+  const float lim = __builtin_fminf(T, 6.0f * X);
   uint32_t mb = 0;
   float c[kGroup];
 #pragma unroll
   for (int i = 0; i < kGroup; ++i) {
-    const bool clipped = __builtin_fabsf(y[i]) > T;
-    c[i] = clipped ? __builtin_copysignf(T, y[i]) : y[i];
-    mb |= (clipped ? 1u : 0u) << i;
+    const float a = __builtin_fabsf(y[i]);
+    c[i] = a > T ? __builtin_copysignf(T, y[i]) : y[i];
+    mb |= (a > lim ? 1u : 0u) << i;
   }
   mbits = mb;
 #pragma unroll

@@ -8,9 +8,17 @@
  * ---------------------------------------
  * - Pointers named x, w, dy, codes, scales, c, y, dx, dw, ws and tensor_scale
  *   are DEVICE pointers owned by the caller.  The library never allocates or
- *   frees memory, holds no mutable global state, and only enqueues work on
- *   `stream` (a hipStream_t; NULL = the default stream).  Calls are
- *   asynchronous: outputs are valid once the stream has been synchronised.
+ *   frees memory and only enqueues work on `stream` (a hipStream_t; NULL =
+ *   the default stream).  Calls are asynchronous: outputs are valid once the
+ *   stream has been synchronised.  No state carries from one call to the
+ *   next except per-device caches of two device queries (the architecture
+ *   check and the compute-unit count), each written once per device and safe
+ *   to read from any thread.
+ * - Device check: a current device other than gfx950 gives FP4MX_E_DEVICE.
+ *   The environment variable FP4MX_DEVICE_ARCH, when set to another
+ *   architecture name, makes every compute call return FP4MX_E_DEVICE after
+ *   argument validation and before any HIP call (a host-only test of the
+ *   refusal); unset or "gfx950", it has no effect.
  * - Every call returns an fp4mx_status.  Arguments are validated on the host
  *   before any launch; on a validation error nothing is enqueued.  A HIP
  *   launch error returns FP4MX_E_HIP and fp4mx_last_hip_error() gives the HIP
@@ -213,6 +221,22 @@ FP4MX_API int fp4mx_linear_bwd(const void* dy, const fp4mx_ctx* ctx, int64_t m, 
                      int64_t k, float* dx, float* dw, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* fp4mx_linear_fwd and fp4mx_linear_bwd with bf16 outputs: y [m][n], dx
+ * [m][k] and dw [n][k] hold bf16 bits, each the round-to-nearest-even of the
+ * fp32 value the fp32 entry point writes (the GEMMs' bf16 epilogue, as in
+ * fp4mx_gemm_bf16).  Arguments, context, workspace and errors as the fp32
+ * forms; outputs 16-B aligned.  These let a bf16 training graph keep every
+ * step of the layer in the library (no separate cast pass).
+ * Source: "Quartet II ..." -- "The Complete Quartet II Computation Graph"
+ * (the layer's outputs and gradients are bf16 tensors between the FP4
+ * GEMMs); the rounding step is this library's design. */
+FP4MX_API int fp4mx_linear_fwd_bf16(const void* x, const void* w, int64_t m, int64_t n,
+                                    int64_t k, uint64_t seed, uint16_t* y, const fp4mx_ctx* ctx,
+                                    void* ws, size_t ws_bytes, void* stream);
+FP4MX_API int fp4mx_linear_bwd_bf16(const void* dy, const fp4mx_ctx* ctx, int64_t m, int64_t n,
+                                    int64_t k, uint16_t* dx, uint16_t* dw, void* ws,
+                                    size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * QuEST forward and the Quartet backward in the forward-rotated basis
  * (source: "Quartet: Native FP4 Training Can Be Optimal for Large Language
@@ -226,10 +250,11 @@ FP4MX_API int fp4mx_linear_bwd(const void* dy, const fp4mx_ctx* ctx, int64_t m, 
 /* QuEST MXFP4 quantization along rows after the block-32 RHT (sign_mask):
  * per 32-group, sigma = standard deviation about the group mean (evaluated on
  * the group scaled by 2^-E, 2^E <= max|y| < 2^(E+1)), T = clip * sigma, E8M0
- * scale floor(log2 T) - 2 (0 when T = 0), codes = E2M1 RNE of the group
- * clamped to [-T, T], mask bit = |y| > T.  A non-finite group gets scale 0xFF,
- * codes 0 and mask 0.  clip must be finite and > 0; the Gaussian RMSE
- * optimum of the page's objective is 2.922475.
+ * scale e = floor(log2 T) - 2 (0 when T = 0, at most 254), codes = E2M1 RNE
+ * of the group clamped to [-T, T] at scale X = 2^(e-127), mask bit =
+ * |y| > min(T, 6 X) (clipped by the clamp or by the grid's end).  A
+ * non-finite group gets scale 0xFF, codes 0 and mask 0.  clip must be finite
+ * and > 0; the Gaussian RMSE optimum of the page's objective is 2.922475.
  *   x bf16 [rows][ld]; codes [rows][cols/2]; scales [rows][cols/32];
  *   mask [rows][cols/8].  Errors as fp4mx_quantize; E_ARG for a bad clip. */
 FP4MX_API int fp4mx_quest_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, float clip,

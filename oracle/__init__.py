@@ -32,8 +32,11 @@ inverse, mask correction, re-quantization and the whole backward unbiased),
 and the Quartet II graph with re-quantized saved NVFP4 operands (de-quantization
 as the rounded exact product, Table 1's MS-EDEN error on re-quantized
 operands, unbiased backward).
-Parity unpinned: the FP8 staging of the NVFP4 GEMM (a design of this library
-that the pages do not describe; only its self-consistency is checked).
+The FP8 staging of the NVFP4 GEMM is a design of this library that the pages
+do not describe; it is pinned exhaustively (every E2M1 code under every pair of
+positive finite E4M3 group scales of a 32-block) against an independent route:
+a brute-force block exponent, the exact product and torch's float8_e4m3fn
+rounding.
 """
 
 from . import formats, rng, rht, mx, nvfp4, msedn, quest, quartet2  # noqa: F401

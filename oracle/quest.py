@@ -15,7 +15,9 @@ Models"):
   the minimisation analytic.
 * "The GPU Kernel Implementation: Two-Stage Fused Design", Stage 1: on the
   forward pass the value that is encoded as the E8M0 power of two is the one
-  the clip factor determines; the mask bit is set iff |x| > c sigma.
+  the clip factor determines; the mask bit is set iff |x| > c sigma (under
+  the page's scale c sigma / 6, c sigma is also where the grid ends; see the
+  mask reading below).
 * "The Hadamard Transform: Why It Is Necessary and How It Is Implemented",
   inverse Hadamard and clipping-mask correction: dx = 16/9 H^-1(dx_q o M_x),
   and the same for dW with M_w; the mask removes the gradient of clipped
@@ -40,14 +42,22 @@ Readings taken (the pages leave these open or disagree):
   level by level in index order.  T = fl(T_z 2^E) (may be +inf, then nothing
   clips).
 * The E8M0 scale encodes T by the rule of the MX path (floor(log2 T) - 2):
-  code = max(floor(log2 T_z) + E + 125, 0), code 0 when T_z = 0.  With this
-  rule QuEST's MSE on N(0,1) is below AbsMax RTN's, the ranking the page
-  reports; taking the scale from min(amax, T) instead would invert it.
-* Clamp: an element with |y| > T becomes sign(y) T (mask bit 1), others are
-  kept (mask bit 0); v = fl(clamped * 2^(127 - code)); code = E2M1 RNE,
-  saturating, sign bit kept.  A group with sigma = 0 (for example one nonzero
-  input in a Hadamard block, which makes the rotated group constant) has
-  T = 0: every nonzero element is clipped to 0 and masked.
+  code = max(floor(log2 T_z) + E + 125, 0), code 0 when T_z = 0, at most 254
+  (a T_z that overflowed to inf gives 254).  With this rule QuEST's MSE on
+  N(0,1) is below AbsMax RTN's, the ranking the page reports; taking the
+  scale from min(amax, T) instead would invert it.
+* Clamp: an element with |y| > T becomes sign(y) T, others are kept;
+  v = fl(clamped * 2^(127 - code)); code = E2M1 RNE, saturating, sign bit
+  kept.  A group with sigma = 0 (for example one nonzero input in a Hadamard
+  block, which makes the rotated group constant) has T = 0: every nonzero
+  element is clipped to 0 and masked.
+* Mask.  The page's scale c sigma / 6 maps [-c sigma, c sigma] onto the grid's
+  range, and the mask flags the elements that were clipped.  With a
+  power-of-two scale X the grid ends at 6 X, and T / X lies in [4, 8), so when
+  T > 6 X the elements with 6 X < |y| <= T are clipped by the saturating
+  rounding instead of the clamp.  Reading: the effective clip is min(T, 6 X)
+  and the mask bit is |y| > min(T, 6 X) (compared exactly; 6 X beyond the
+  fp32 range clips nothing).
 * A non-finite group (after the transform) gets scale 0xFF, element codes 0
   and mask bits 0, as on the MX path.
 * The page multiplies dx_q by M_x while saying the mask zeroes the gradient of
@@ -176,15 +186,20 @@ def quest_quantize(x: np.ndarray, sign_mask: int, clip: float, hadamard: bool = 
         var = (_tree((d * d).astype(np.float32)) * np.float32(0.03125)).astype(np.float32)
         sig = np.sqrt(var).astype(np.float32)
         tz = (np.float32(clip) * sig).astype(np.float32)
-        code = np.where(tz > 0, np.maximum(_floor_log2(np.where(tz > 0, tz, 1)) + E + 125, 0), 0)
+        ok = (tz > 0) & np.isfinite(tz)
+        code = np.where(ok, _floor_log2(np.where(ok, tz, 1)) + E + 125, 0)
+        code = np.where(np.isinf(tz), 254, np.clip(code, 0, 254))
         T = np.ldexp(tz, E).astype(np.float32)
         clipped = np.abs(gs) > T[..., None]
         cl = np.where(clipped, np.copysign(np.broadcast_to(T[..., None], gs.shape), gs), gs)
         inv = np.ldexp(np.float32(1.0), (127 - code).astype(np.int32)).astype(np.float32)
         v = (cl.astype(np.float32) * inv[..., None]).astype(np.float32)
+        # the effective clip is min(T, 6 X): beyond 6 X the E2M1 grid saturates
+        lim = np.minimum(T.astype(np.float64), 6.0 * np.ldexp(1.0, code.astype(np.int64) - 127))
+        masked = np.abs(gs.astype(np.float64)) > lim[..., None]
     q = formats.e2m1_rtn(v)
     q = np.where(finite[..., None], q, 0).astype(np.uint8).reshape(R, C)
-    clipped = np.where(finite[..., None], clipped, False).reshape(R, C)
+    clipped = np.where(finite[..., None], masked, False).reshape(R, C)
     code = np.where(finite, code, 255).astype(np.uint8)
     packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
     mask = np.packbits(clipped, axis=1, bitorder="little")

@@ -68,3 +68,53 @@ def edge_case_tensor(rows: int, cols: int, seed: int = 0) -> np.ndarray:
         if i * 7 < flat.shape[0]:
             flat[i * 7] = np.asarray(b, dtype=np.float32)
     return synth.f32_to_bf16_bits(flat.reshape(rows, cols))
+
+
+# ---------------------------------------------------------------------------
+# Element-wise GEMM check.
+#
+# The FP4 GEMM multiplies E2M1 values scaled by powers of two (each product is
+# exact) and accumulates in fp32: every MFMA adds a 64-element K slice to the
+# fp32 accumulator.  Modelling each MFMA as at most two fp32 roundings of a
+# partial sum bounded by S = sum_k |a_ik b_jk|, plus one rounding for alpha and
+# one for alpha's own fp32 value, gives
+#     |C_gpu - alpha C_64| <= u (K/32 + 4) |alpha| S,   u = 2^-24.
+# The check uses twice that, u (K/16 + 8) |alpha| S, so every output element
+# is held to a few fp32 ulps of its own magnitude scale; a wrong group scale,
+# a misplaced tile or a dropped K slice moves elements by far more.
+# ---------------------------------------------------------------------------
+
+def gemm_bound_factor(k: int) -> float:
+    return 2.0 ** -24 * (k / 16 + 8)
+
+
+def assert_gemm_close(got, a64, b64, alpha, what, tol=1e-5, extra_bound=None):
+    """got [M,N] (fp32 from the GPU) against alpha * a64 @ b64^T in fp64:
+    element-wise within the accumulation bound (plus ``extra_bound`` [M,N] if
+    given) and within ``tol`` relative Frobenius.  Non-finite expected entries
+    must match (NaN for NaN)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = alpha * (a64 @ b64.T)
+    S = abs(alpha) * (np.abs(a64) @ np.abs(b64).T)
+    bound = gemm_bound_factor(a64.shape[1]) * S
+    if extra_bound is not None:
+        bound = bound + extra_bound
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isnan(got[~fin]), np.isnan(want[~fin])), what + ": non-finite entries differ"
+    err = np.abs(got[fin] - want[fin])
+    b = bound[fin]
+    bad = err > b
+    ratio = float(np.max(err / np.where(b > 0, b, 1.0))) if err.size else 0.0
+    fro = rel_fro(got[fin], want[fin])
+    log("  %s: max err/bound %.3f, rel fro %.2e, %d elements" % (what, ratio, fro, err.size))
+    if bad.any():
+        i = np.argmax(bad)
+        raise AssertionError("%s: %d of %d elements beyond the bound; first at flat %d: got %r want %r "
+                             "bound %r" % (what, int(bad.sum()), bad.size, i, got[fin][i], want[fin][i], b[i]))
+    assert fro <= tol, (what, fro)
+
+
+def edge_case_tensor_cols(rows: int, cols: int, seed: int = 0) -> np.ndarray:
+    """edge_case_tensor with its special 32-blocks running down columns: the
+    column-axis quantizer sees them as whole groups."""
+    return np.ascontiguousarray(edge_case_tensor(cols, rows, seed).T)

@@ -166,3 +166,32 @@ def test_nv_requant_and_ctx_validation():
     bad = binding.NvCtxStruct(p.value, p.value + 1, p.value, p.value, p.value, p.value, 0)
     assert L.fp4nv_linear_bwd_ctx(p, C.byref(bad), 128, 128, 64, f, f, p, 1 << 26, None) == -3
     assert L.fp4nv_linear_bwd_ctx(p, None, 128, 128, 64, f, f, p, 1 << 26, None) == -1
+
+
+def test_non_gfx950_device_is_refused():
+    """FP4MX_DEVICE_ARCH stands in for the device query: with another
+    architecture every compute call returns FP4MX_E_DEVICE after validating
+    its arguments and before any HIP call, so this runs without a GPU.  A
+    fresh process reads the variable."""
+    import subprocess
+    import sys
+    prog = r'''
+import ctypes as C, sys
+sys.path.insert(0, %r)
+from fp4_microscaled_quantized_amd import binding
+L = binding.lib()
+b = C.create_string_buffer(1 << 16)
+p = C.c_void_p((C.addressof(b) + 255) & ~255)
+out = [
+    L.fp4mx_quantize(p, 64, 64, 64, 0, 0, 0, 0, p, p, None),
+    L.fp4mx_gemm(p, p, p, p, 64, 64, 64, C.c_float(1.0), p, 64, None),
+    L.fp4nv_quantize46(p, 64, 64, 64, 1, p, p, p, p, 256, None),
+    L.fp4mx_quantize(None, 64, 64, 64, 0, 0, 0, 0, p, p, None),   # validation still first
+]
+print(" ".join(str(v) for v in out))
+''' % ROOT
+    env = dict(os.environ, FP4MX_DEVICE_ARCH="gfx942")
+    r = subprocess.run([sys.executable, "-c", prog], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["-6", "-6", "-6", "-1"]
+    assert binding.lib().fp4mx_status_string(-6) == b"device is not gfx950"

@@ -7,7 +7,7 @@ import fp4_microscaled_quantized_amd as fq
 from fp4_microscaled_quantized_amd import synth
 from oracle import mx
 
-from gpu_util import cpu, dev_bf16, host_f32, log, rel_fro
+from gpu_util import assert_gemm_close, cpu, dev_bf16, host_f32, log, rel_fro
 
 pytestmark = pytest.mark.gpu
 
@@ -35,10 +35,25 @@ def test_gemm_parity(m, n, k):
     qb = mx.quantize(host_f32(b), rounding=mx.SR, sign_mask=3, seed=1, stream=2)
     c = fq.gemm(_to_dev_mx(*qa), _to_dev_mx(*qb), alpha=1.5)
     torch.cuda.synchronize()
-    want = mx.gemm(*qa, *qb, alpha=1.5)
-    err = rel_fro(cpu(c), want)
-    log("  rel err", err)
-    assert err <= TOL
+    assert_gemm_close(cpu(c), mx.dequantize(*qa), mx.dequantize(*qb), 1.5, "gemm %dx%dx%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 1024, 512), (1024, 2048, 256), (1056, 1824, 320),
+                                   (2048, 1024, 1024)])
+def test_gemm_parity_xcd_remap(m, n, k):
+    """Shapes whose 256 x 256 tile count is a multiple of 8 (8, 32, 40 and 32
+    tiles), so the launch takes the XCD-aware tile order; one is ragged in M,
+    N and K.  C starts as NaN: an unwritten or twice-mapped tile fails."""
+    log("gemm remap", m, n, k, "tiles", -(-m // 256) * -(-n // 256))
+    a, b = _operands(m, n, k, seed=2)
+    qa = mx.quantize(host_f32(a), rounding=mx.SR, sign_mask=7, seed=5, stream=1)
+    qb = mx.quantize(host_f32(b), rounding=mx.RTN, sign_mask=7)
+    out = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    fq.gemm(_to_dev_mx(*qa), _to_dev_mx(*qb), alpha=16 / 9, out=out)
+    torch.cuda.synchronize()
+    c = cpu(out)
+    assert np.all(np.isfinite(c))
+    assert_gemm_close(c, mx.dequantize(*qa), mx.dequantize(*qb), mx.ALPHA_BWD, "remap %dx%dx%d" % (m, n, k))
 
 
 def test_gemm_output_stride_and_alpha():
@@ -50,7 +65,7 @@ def test_gemm_output_stride_and_alpha():
     torch.cuda.synchronize()
     o = cpu(out)
     assert np.all(o[:, 96:] == 7.0)               # columns beyond n untouched
-    assert rel_fro(o[:, :96], mx.gemm(*qa, *qb, alpha=16 / 9)) <= TOL
+    assert_gemm_close(o[:, :96], mx.dequantize(*qa), mx.dequantize(*qb), 16 / 9, "strided out")
 
 
 def test_gemm_nan_scale_propagates():
@@ -70,7 +85,7 @@ def test_gemm_extreme_scales():
     qa = (rs.integers(0, 256, (64, 64), dtype=np.uint8), rs.integers(100, 150, (64, 4)).astype(np.uint8))
     qb = (rs.integers(0, 256, (32, 64), dtype=np.uint8), rs.integers(100, 150, (32, 4)).astype(np.uint8))
     c = cpu(fq.gemm(_to_dev_mx(*qa), _to_dev_mx(*qb)))
-    assert rel_fro(c, mx.gemm(*qa, *qb)) <= TOL
+    assert_gemm_close(c, mx.dequantize(*qa), mx.dequantize(*qb), 1.0, "extreme scales")
 
 
 def _bf16_rne_bits(f32):

@@ -12,7 +12,7 @@ import fp4_microscaled_quantized_amd as fq
 from fp4_microscaled_quantized_amd import synth
 from oracle import mx, rng
 
-from gpu_util import assert_bytes_equal, cpu, dev_bf16, host_f32, log, rel_fro
+from gpu_util import assert_bytes_equal, assert_gemm_close, cpu, dev_bf16, host_f32, log, rel_fro
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -51,6 +51,16 @@ def test_forward_backward_small(m, n, k):
     assert_bytes_equal(cpu(ctx.xt.scales), rctx["xt"][1], "ctx xt scales")
     assert_bytes_equal(cpu(ctx.wt.codes), rctx["wt"][0], "ctx wt codes")
     assert_bytes_equal(cpu(ctx.wt.scales), rctx["wt"][1], "ctx wt scales")
+    # the layer's GEMM operands, each from the oracle's quantizer
+    g0, g1, g2 = (rng.sign_mask(seed, i) for i in range(3))
+    deq = lambda q: mx.dequantize(*q)
+    qx = mx.quantize(xf, rounding=mx.RTN, sign_mask=g0)
+    qw = mx.quantize(wf, rounding=mx.RTN, sign_mask=g0)
+    qdy = mx.quantize(dyf, rounding=mx.SR, sign_mask=g1, seed=seed, stream=1)
+    qdyt = mx.quantize(dyf, rounding=mx.SR, axis=mx.COL, sign_mask=g2, seed=seed, stream=3)
+    assert_gemm_close(cpu(y), deq(qx), deq(qw), 1.0, "y")
+    assert_gemm_close(cpu(dx), deq(qdy), deq(rctx["wt"]), mx.ALPHA_BWD, "dx")
+    assert_gemm_close(cpu(dw), deq(qdyt), deq(rctx["xt"]), mx.ALPHA_BWD, "dw")
     rdx, rdw = mx.linear_bwd(dyf, rctx)
     for name, got, want in (("y", y, ry), ("dx", dx, rdx), ("dw", dw, rdw)):
         err = rel_fro(cpu(got), want)
@@ -122,6 +132,29 @@ def test_quartet_workload_full_size():
 
 def test_llama_ffn_up_workload_full_size():
     _sampled_full_size(synth.llama_ffn_up(0), seed=0)
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 96, 160), (256, 384, 512)])
+def test_bf16_output_entry_points(m, n, k):
+    """fp4mx_linear_fwd_bf16 / _bwd_bf16 write bf16_RNE of what the fp32
+    entry points write, bit for bit, and share their context bytes."""
+    log("linear bf16 out", m, n, k)
+    xb = synth.normal_with_outliers((m, k), 5, 0)
+    wb = synth.normal((n, k), 0.02, 5, 1)
+    dyb = synth.normal((m, n), 1e-3, 5, 2)
+    x, w, dy = dev_bf16(xb), dev_bf16(wb), dev_bf16(dyb)
+    y32, c32 = fq.linear_fwd(x, w, seed=8)
+    dx32, dw32 = fq.linear_bwd(dy, c32)
+    y16, c16 = fq.linear_fwd(x, w, seed=8, dtype=torch.bfloat16)
+    dx16, dw16 = fq.linear_bwd(dy, c16, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    bits = lambda t: cpu(t.view(torch.int16)).view(np.uint16)
+    for a, b in ((c16.xt, c32.xt), (c16.wt, c32.wt)):
+        assert_bytes_equal(cpu(a.codes), cpu(b.codes), "ctx codes")
+        assert_bytes_equal(cpu(a.scales), cpu(b.scales), "ctx scales")
+    for name, got, want in (("y", y16, y32), ("dx", dx16, dx32), ("dw", dw16, dw32)):
+        assert got.dtype == torch.bfloat16
+        assert_bytes_equal(bits(got), synth.f32_to_bf16_bits(cpu(want)), name + " bf16")
 
 
 def test_autograd_function():

@@ -7,7 +7,7 @@ import fp4_microscaled_quantized_amd as fq
 from fp4_microscaled_quantized_amd import synth
 from oracle import mx, rng
 
-from gpu_util import assert_bytes_equal, cpu, dev_bf16, edge_case_tensor, host_f32, log
+from gpu_util import assert_bytes_equal, cpu, dev_bf16, edge_case_tensor, edge_case_tensor_cols, host_f32, log
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +44,35 @@ def test_quantize_small(shape, axis, rounding, had):
 def test_quantize_edge_cases(axis, rounding, had):
     bits = edge_case_tensor(128, 256)
     _check(bits, axis, rounding, had, what="edge")
+
+
+@pytest.mark.parametrize("rounding", [fq.RTN, fq.SR])
+@pytest.mark.parametrize("had", [True, False])
+@pytest.mark.parametrize("shape", [(256, 128), (160, 96)])
+def test_quantize_edge_cases_along_columns(rounding, had, shape):
+    """The special groups planted down columns, so the column-axis quantizer
+    meets whole zero, -0, subnormal, huge, tie, NaN and Inf groups."""
+    bits = edge_case_tensor_cols(*shape, seed=2)
+    _check(bits, fq.COL, rounding, had, what="edge-col")
+
+
+@pytest.mark.parametrize("rr,cr", [(fq.RTN, fq.SR), (fq.SR, fq.SR), (fq.RTN, fq.RTN), (fq.SR, fq.RTN)])
+@pytest.mark.parametrize("planted", ["rows", "cols"])
+def test_dual_edge_cases(rr, cr, planted):
+    """Dual kernel on tensors whose special groups run along rows or along
+    columns: both outputs equal the oracle's single-axis quantizers."""
+    bits = edge_case_tensor(256, 192, 6) if planted == "rows" else edge_case_tensor_cols(256, 192, 6)
+    seed, m1, m2 = 3, 0x0F0F1234, 0xA5A5A5A5
+    log("dual edge", planted, rr, cr)
+    ro, co = fq.hadamard_quantize_dual(dev_bf16(bits), rr, m1, 1, cr, m2, 3, seed=seed)
+    torch.cuda.synchronize()
+    xf = host_f32(bits)
+    wr = _oracle(xf, mx.ROW, rr, True, m1, seed, 1)
+    wc = _oracle(xf, mx.COL, cr, True, m2, seed, 3)
+    assert_bytes_equal(cpu(ro.codes), wr[0], "dual row codes")
+    assert_bytes_equal(cpu(ro.scales), wr[1], "dual row scales")
+    assert_bytes_equal(cpu(co.codes), wc[0], "dual col codes")
+    assert_bytes_equal(cpu(co.scales), wc[1], "dual col scales")
 
 
 def test_quantize_mask_zero_is_plain_hadamard():
@@ -86,9 +115,10 @@ def test_quantizer_workload_full_size_row(rounding):
     _check(bits, fq.ROW, rounding, True, mask=mask, seed=0, stream=1, what="c2-full")
 
 
-def test_quantizer_workload_full_size_col_sr():
+@pytest.mark.parametrize("rounding", [fq.RTN, fq.SR])
+def test_quantizer_workload_full_size_col(rounding):
     bits = synth.quantizer_tensor()["x"]
-    _check(bits, fq.COL, fq.SR, True, mask=rng.sign_mask(0, 0), seed=0, stream=1, what="c2-full-col")
+    _check(bits, fq.COL, rounding, True, mask=rng.sign_mask(0, 0), seed=0, stream=1, what="c2-full-col")
 
 
 def test_col_axis_scales_at_odd_address():

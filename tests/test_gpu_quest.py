@@ -38,6 +38,15 @@ def test_quest_clip_values(clip):
     _check_quest(synth.normal_and_student_t((128, 512), 2, 1), rng.sign_mask(2, 0), clip)
 
 
+@pytest.mark.parametrize("clip", [8.0, 1e3, 3.0e38])
+def test_quest_scale_saturates(clip):
+    """Thresholds beyond the E8M0 range encode as 254, on both sides."""
+    log("quest huge threshold", clip)
+    rs = np.random.default_rng(15)
+    x = (rs.standard_normal((64, 256)) * 1e36).astype(np.float32)
+    _check_quest(synth.f32_to_bf16_bits(x), rng.sign_mask(15, 0), clip)
+
+
 def test_quest_edge_cases():
     log("quest edge cases")
     _check_quest(edge_case_tensor(128, 256, 3), rng.sign_mask(3, 0), CLIP)

@@ -195,3 +195,74 @@ def test_linear_backward_unbiased_1_over_B():
     for ests, ex in ((sums_dx, ex_dx), (sums_dw, ex_dw)):
         e1, e16, e64 = mse(ests, ex, 1), mse(ests, ex, 16), mse(ests, ex, 64)
         assert e16 < e1 / 8 and e64 < e1 / 30
+
+
+def test_sr_truncation_bias_on_gradient_operand(monkeypatch):
+    """The 22-bit SR rule's bias, measured on a real gradient operand.
+
+    Rows of the Quartet workload's dY (8192 x 4096, N(0, 1e-3)) are quantized
+    as the backward's dY operand (RHT along N with GEMM 1's mask, SR of the
+    3/4-prescaled group).  The oracle's quantizer is run as a black box with
+    the 32-bit draw of every element forced to a chosen value: the rounding
+    decision is monotone in the draw's top 22 bits, so a binary search over
+    them finds, per element, how many of the 2^22 draws round up, and with it
+    the exact expectation of the decoded value.  The bias E[deq] - 0.75 y is
+    then compared with the SR noise that the 1/B unbiasedness tests average
+    away (B up to 256)."""
+    from fp4_microscaled_quantized_amd import synth
+    rows = synth.normal((8192, 4096), 1e-3, 0, synth.TENSOR_DY)[::128]     # 64 rows, 262144 elements
+    y_in = synth.bf16_bits_to_f32(rows)
+    g1 = rng.sign_mask(0, 1)
+    draws = {}
+
+    def forced_bits(seed, stream, idx):
+        return np.broadcast_to(draws["r"], np.shape(idx)).astype(np.uint32)
+
+    monkeypatch.setattr(rng, "bits", forced_bits)
+
+    def deq_with(r):
+        draws["r"] = np.asarray(r, dtype=np.uint32).reshape(64, 128, 32)
+        return mx.dequantize(*mx.quantize(y_in, rounding=mx.SR, sign_mask=g1, seed=0, stream=1))
+
+    shape = y_in.shape
+    down = deq_with(np.zeros(shape, np.uint32))                       # every element rounds down
+    up = deq_with(np.full(shape, 0xFFFFFC00, np.uint32))              # draw 2^22 - 1: up where p > 0
+    # smallest 22-bit draw j* that rounds up (2^22 if none): binary search
+    lo = np.zeros(shape, np.int64)
+    hi = np.full(shape, 1 << 22, np.int64)
+    while np.any(lo < hi):
+        mid = (lo + hi) // 2
+        d = deq_with((np.minimum(mid, (1 << 22) - 1) << 10).astype(np.uint32))
+        goes_up = (d != down) & (mid < (1 << 22))
+        hi = np.where(goes_up, mid, hi)
+        lo = np.where(goes_up, lo, mid + 1)
+    n_up = (1 << 22) - hi
+    # monotonicity (the premise of the search) at random draws
+    rs = np.random.default_rng(3)
+    for _ in range(4):
+        j = rs.integers(0, 1 << 22, shape)
+        d = deq_with((j << 10).astype(np.uint32))
+        assert np.array_equal(d != down, j >= hi)
+    ed = down + (up - down) * (n_up / 2.0 ** 22)                      # exact E[deq]
+    y = rht.rht32(y_in, g1).astype(np.float64)
+    X = np.repeat(mx.quantize(y_in, rounding=mx.SR, sign_mask=g1)[1], 32, axis=1)
+    X = formats.e8m0_value(X)
+    bias = ed - 0.75 * y
+    gap = np.abs(up - down)
+    sub1 = np.abs(0.75 * y) < X
+    # |v| >= 1: unbiased up to the one rounding of the prescale fl(0.75 y 2^k)
+    pre = 2.0 ** -24 * np.abs(0.75 * y)
+    assert np.all(np.abs(bias[~sub1]) <= pre[~sub1])
+    # |v| < 1: toward zero by less than 2^-22 of the gap (0.5 X), plus the prescale
+    assert np.all(np.abs(bias[sub1]) <= 2.0 ** -22 * gap[sub1] + pre[sub1])
+    assert np.all(np.abs(bias) <= 2.0 ** -23 * X + pre)
+    assert sub1.mean() > 0.2                                          # the case is common
+    # SR noise per element: the std of the rounding, sqrt(p (1 - p)) * gap
+    p = np.where(gap > 0, np.abs(ed - down) / np.where(gap > 0, gap, 1), 0.0)
+    noise = np.sqrt(p * (1 - p)) * gap
+    rms_bias, rms_noise = np.sqrt(np.mean(bias ** 2)), np.sqrt(np.mean(noise ** 2))
+    for B in (1, 16, 64, 256):
+        assert rms_bias < 1e-3 * rms_noise / math.sqrt(B), (B, rms_bias, rms_noise)
+    # the operand-level systematic error is far below the B = 256 mean's noise too
+    print("rms bias %.3e  rms noise %.3e  mean bias %.3e  sub1 %.3f" % (rms_bias, rms_noise, np.mean(bias), sub1.mean()))
+    assert abs(np.mean(bias)) < 1e-3 * rms_noise / math.sqrt(256 * bias.size)

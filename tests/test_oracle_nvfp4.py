@@ -65,3 +65,49 @@ def test_fp8_staging_range_and_accuracy():
     st2, e2 = nvfp4.fp8_stage(codes, scales)
     full = st2 * np.ldexp(1.0, np.repeat(e2, 32, axis=1))
     assert np.array_equal(full, nvfp4.dequantize(codes, scales, 1.0))
+
+
+def test_fp8_staging_exhaustive_against_torch():
+    """Every (E2M1 code, positive finite E4M3 scale of its group, scale of the
+    other group in the 32-block) staged as the library's FP8 GEMM expects,
+    against an independent route: the block exponent from a brute-force search
+    for each scale's power of two, the product q * s16 * 2^-e_blk formed
+    exactly (at most 6 significant bits, so exact in fp32), and the E4M3
+    rounding done by torch's float8_e4m3fn conversion."""
+    import torch
+    scales = np.arange(0x7F, dtype=np.uint8)                  # 0 .. 0x7E: +0 and every positive finite E4M3
+    sa, sb = np.meshgrid(scales, scales, indexing="ij")
+    sa, sb = sa.ravel(), sb.ravel()                           # 16129 scale pairs, one block row each
+    rows = sa.size
+    nib = np.arange(16, dtype=np.uint8)
+    half = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)    # the 16 codes of one 16-group, packed
+    codes = np.tile(np.concatenate([half, half]), (rows, 1))  # [rows, 16] bytes = 32 elements
+    sc = np.stack([sa, sb], axis=1)                           # [rows, 2] E4M3 bytes
+    got_b, got_e = nvfp4.fp8_stage_bytes(codes, sc)
+
+    # independent route
+    def pow2_floor(s):
+        """largest e with 2^e <= s, by search (None for 0)."""
+        if s == 0:
+            return None
+        e = -30
+        while 2.0 ** (e + 1) <= s:
+            e += 1
+        return e
+    val = {int(c): float(formats.e4m3_decode(np.array([c]))[0]) for c in scales}
+    pe = {c: pow2_floor(v) for c, v in val.items()}
+    e_blk = np.empty(rows, np.int64)
+    for i, (a, b) in enumerate(zip(sa, sb)):
+        es = [e for e in (pe[int(a)], pe[int(b)]) if e is not None]
+        e_blk[i] = max(es) - 5 if es else 0
+    assert np.array_equal(got_e[:, 0], e_blk)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    qv = np.where(nib & 8, -grid[nib & 7], grid[nib & 7])       # the 16 code values
+    s16 = np.stack([np.vectorize(val.get)(sa), np.vectorize(val.get)(sb)], axis=1).astype(np.float64)
+    prod = qv[None, None, :] * s16[:, :, None] * np.ldexp(1.0, -e_blk)[:, None, None]
+    p32 = prod.astype(np.float32)
+    assert np.array_equal(p32.astype(np.float64), prod)        # exact before the FP8 rounding
+    want = torch.from_numpy(p32.reshape(rows, 32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got_b, want)
+    # the staged magnitudes stay inside E4M3's range: at most 6 * 1.875 * 2^5
+    assert np.abs(prod).max() == 360.0

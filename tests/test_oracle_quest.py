@@ -101,9 +101,34 @@ def test_scales_and_mask_against_fp64():
     want = np.floor(lg).astype(np.int64) + 125
     assert np.all(sc.astype(np.int64)[safe] == want[safe])
     bits = quest.unpack_mask(mask, 512).reshape(128, 16, 32)
-    far = np.abs(np.abs(y) - T64[..., None]) > 1e-5 * T64[..., None]
-    assert np.array_equal(bits[far], (np.abs(y) > T64[..., None])[far])
-    assert 0.0005 < bits.mean() < 0.02
+    lim = np.minimum(T64, 6.0 * np.ldexp(1.0, sc.astype(np.int64) - 127))
+    far = np.abs(np.abs(y) - lim[..., None]) > 1e-5 * lim[..., None]
+    assert np.array_equal(bits[far], (np.abs(y) > lim[..., None])[far])
+    assert 0.0005 < bits.mean() < 0.05
+
+
+def test_mask_covers_every_saturated_element():
+    """With a power-of-two scale X the grid ends at 6 X while T / X lies in
+    [4, 8): an element beyond 6 X is clipped by the saturating rounding even
+    when it is below T, and its gradient must be masked like a clamped one."""
+    x = _bf16(np.random.default_rng(12).standard_t(4, (256, 512)))
+    m, c = rng.sign_mask(13, 0), quest.optimal_clip()
+    codes, sc, mask = quest.quest_quantize(x, m, c)
+    y = rht.rht32(x, m).astype(np.float64).reshape(256, 16, 32)
+    _, T = quest.group_sigma_threshold(x, m, c)
+    X = np.ldexp(1.0, sc.astype(np.int64) - 127)
+    bits = quest.unpack_mask(mask, 512).reshape(256, 16, 32)
+    beyond_grid = np.abs(y) > 6.0 * X[..., None]
+    beyond_T = np.abs(y) > T.astype(np.float64)[..., None]
+    # both kinds of clipping occur, and T > 6 X in a good share of the groups
+    assert beyond_grid.any() and beyond_T.any()
+    assert 0.2 < np.mean(T > 6.0 * X) < 0.7
+    assert np.all(bits[beyond_grid]) and np.all(bits[beyond_T])
+    assert np.array_equal(bits, beyond_grid | beyond_T)
+    # an element that is not masked is represented without saturation:
+    # its magnitude code is below 6, or it rounded to 6 from at most 6 X
+    q = mx.unpack(codes).reshape(256, 16, 32) & 7
+    assert np.all(np.abs(y)[(q == 7) & ~bits] <= 6.0 * X[..., None].repeat(32, 2)[(q == 7) & ~bits])
 
 
 def test_clipped_groups_reduce_to_mx_rtn():
@@ -157,6 +182,24 @@ def test_clip_large_means_no_mask_and_scale_from_T():
     assert not quest.unpack_mask(mask, 128).any()
     sig, T = quest.group_sigma_threshold(x, 0, 1e3)
     assert np.array_equal(sc.astype(np.int64), quest._floor_log2(T) + 125)
+
+
+def test_scale_code_saturates_at_254():
+    """A threshold beyond the E8M0 range gives scale 254 (never a wrapped
+    byte or the 0xFF marker), finite codes and no mask bits."""
+    rs = np.random.default_rng(14)
+    x = _bf16(rs.standard_normal((8, 64)) * 1e36)     # transform sums stay finite
+    for clip in (8.0, 1e3, 3.0e38):
+        codes, sc, mask = quest.quest_quantize(x, 0, clip)
+        _, T = quest.group_sigma_threshold(x, 0, clip)
+        want = np.where(np.isinf(T), 254, np.minimum(quest._floor_log2(np.where(np.isinf(T), 1, T)) + 125, 254))
+        assert np.array_equal(sc.astype(np.int64), want)
+        assert np.all(sc <= 254) and not quest.unpack_mask(mask, 64).any()
+        y = rht.rht32(x, 0).astype(np.float64)
+        deq = mx.dequantize(codes, sc)
+        # no sign flips: every nonzero code has the sign of its element
+        nz = deq != 0
+        assert np.all(np.sign(deq[nz]) == np.sign(y[nz]))
 
 
 # --------------------------- backward pieces --------------------------------
