@@ -83,6 +83,8 @@ _SIGS = {
     "fp4nv_msedn_workspace_bytes": (_SZ, [_I64, _I64]),
     "fp4nv_msedn_quantize": (_INT, [_P, _I64, _I64, _I64, _INT, C.c_float, _U64, _U32, _U32, _P, _P,
                                     _P, _P, _P, _SZ, _P]),
+    "fp4nv_msedn_quantize_noalloc": (_INT, [_P, _I64, _I64, _I64, _INT, C.c_float, _U64, _U32, _U32, _P,
+                                            _P, _P, _P, _P]),
     "fp4nv_linear_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "fp4nv_linear_bwd": (_INT, [_P, _P, _P, _I64, _I64, _I64, _U64, _P, _P, _P, _SZ, _P]),
     "fp4nv_msedn_requantize": (_INT, [_P, _P, _P, _I64, _I64, C.c_float, _U64, _U32, _U32, _P, _P, _P,

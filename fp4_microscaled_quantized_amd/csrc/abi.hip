@@ -132,6 +132,8 @@ const char* fp4mx_status_string(int status) {
     case FP4MX_E_WORKSPACE: return "workspace missing or too small";
     case FP4MX_E_DEVICE: return "device is not gfx950";
     case FP4MX_E_HIP: return "HIP error";
+    case FP4MX_E_SCRATCH:
+      return "input needs more scratch than the no-allocation entry point's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -589,10 +591,9 @@ static int msedn_impl(const void* x, int64_t rows, int64_t cols, int64_t ld, int
   return e == hipSuccess ? FP4MX_OK : hip_fail(e);
 }
 
-int fp4nv_msedn_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis,
-                         float clip_s, uint64_t seed, uint32_t gemm_id, uint32_t rng_stream,
-                         uint8_t* codes, uint8_t* scales, float* tensor_scale, float* eden_s,
-                         void* ws, size_t ws_bytes, void* stream) {
+static int msedn_check(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                       float clip_s, const uint8_t* codes, const uint8_t* scales,
+                       const float* tensor_scale, const float* eden_s) {
   if (!x || !codes || !scales || !tensor_scale) return FP4MX_E_NULL;
   if (!dim_ok(rows) || !dim_ok(cols) || ld < cols) return FP4MX_E_SHAPE;
   if (axis != FP4MX_AXIS_ROW && axis != FP4MX_AXIS_COL) return FP4MX_E_ARG;
@@ -601,12 +602,74 @@ int fp4nv_msedn_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, 
   if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scales & 1u) || ld % 8 != 0 ||
       ((uintptr_t)tensor_scale & 3u) || ((uintptr_t)eden_s & 3u))
     return FP4MX_E_ALIGN;
+  return FP4MX_OK;
+}
+
+int fp4nv_msedn_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                         float clip_s, uint64_t seed, uint32_t gemm_id, uint32_t rng_stream,
+                         uint8_t* codes, uint8_t* scales, float* tensor_scale, float* eden_s,
+                         void* ws, size_t ws_bytes, void* stream) {
+  int st = msedn_check(x, rows, cols, ld, axis, clip_s, codes, scales, tensor_scale, eden_s);
+  if (st) return st;
   if (!ws || ws_bytes < fp4nv_msedn_workspace_bytes(rows, cols)) return FP4MX_E_WORKSPACE;
   if (!aligned16(ws)) return FP4MX_E_ALIGN;
-  int st = check_device();
-  if (st) return st;
+  if ((st = check_device())) return st;
   return msedn_impl(x, rows, cols, ld, axis, clip_s, seed, gemm_id, rng_stream, codes, scales,
                     tensor_scale, eden_s, static_cast<uint8_t*>(ws), (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------- no-allocation MS-EDEN entry ----------------------
+// The library's own scratch for fp4nv_msedn_quantize_noalloc: the fp32 v of
+// every output 16-group and the tensor maximum, in one file-scope device
+// array.  Each GPU the library runs on holds its own copy until the process
+// ends.  Host code never passes `scratch` itself to a kernel (in host code
+// the name is a stand-in, not the device address): the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+namespace {
+
+__device__ __align__(256) uint8_t scratch[FP4MX_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+
+int scratch_ptr(uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return FP4MX_E_DEVICE;
+  uint8_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!q) return FP4MX_E_DEVICE;
+    p = static_cast<uint8_t*>(q);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return FP4MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4nv_msedn_quantize_noalloc(const void* x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                                 float clip_s, uint64_t seed, uint32_t gemm_id,
+                                 uint32_t rng_stream, uint8_t* codes, uint8_t* scales,
+                                 float* tensor_scale, float* eden_s, void* stream) {
+  int st = msedn_check(x, rows, cols, ld, axis, clip_s, codes, scales, tensor_scale, eden_s);
+  if (st) return st;
+  if (fp4nv_msedn_workspace_bytes(rows, cols) > (size_t)FP4MX_NOALLOC_SCRATCH_BYTES)
+    return FP4MX_E_SCRATCH;
+  if ((st = check_device())) return st;
+  uint8_t* p = nullptr;
+  if ((st = scratch_ptr(&p))) return st;
+  // msedn_impl carves the fp32 v buffer and the maximum word from `p`; the
+  // maximum is cleared by a kernel and every v is written before it is read
+  return msedn_impl(x, rows, cols, ld, axis, clip_s, seed, gemm_id, rng_stream, codes, scales,
+                    tensor_scale, eden_s, p, (hipStream_t)stream);
 }
 
 size_t fp4nv_linear_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k) {

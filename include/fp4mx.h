@@ -97,7 +97,9 @@ typedef enum {
   FP4MX_E_ARG = -4,       /* bad enum value or argument combination           */
   FP4MX_E_WORKSPACE = -5, /* workspace NULL or smaller than required          */
   FP4MX_E_DEVICE = -6,    /* current device is not gfx950                     */
-  FP4MX_E_HIP = -7        /* a HIP call failed; see fp4mx_last_hip_error()    */
+  FP4MX_E_HIP = -7,       /* a HIP call failed; see fp4mx_last_hip_error()    */
+  FP4MX_E_SCRATCH = -8    /* the input needs more scratch than the static
+                             buffer of a no-allocation entry point holds      */
 } fp4mx_status;
 
 enum { FP4MX_ROUND_RTN = 0, FP4MX_ROUND_SR = 1 };
@@ -408,6 +410,26 @@ FP4MX_API int fp4nv_msedn_quantize(const void* x, int64_t rows, int64_t cols, in
                          float clip_s, uint64_t seed, uint32_t gemm_id, uint32_t rng_stream,
                          uint8_t* codes, uint8_t* scales, float* tensor_scale, float* eden_s,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* Size of the library's static device scratch (per GPU, held until the
+ * process ends) used by fp4nv_msedn_quantize_noalloc: 32 MiB + 256 B. */
+#define FP4MX_NOALLOC_SCRATCH_BYTES 33554688
+
+/* fp4nv_msedn_quantize without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The scratch (fp32 v per output 16-group
+ * plus the tensor maximum, fp4nv_msedn_workspace_bytes(rows, cols) bytes) is
+ * a file-scope device array of FP4MX_NOALLOC_SCRATCH_BYTES in the library;
+ * inputs needing more get FP4MX_E_SCRATCH (rows * cols up to 2^27
+ * elements fit, e.g. 16384 x 8192).  The call allocates nothing.  Every call
+ * on a GPU shares that GPU's one array: calls that overlap on one GPU (two
+ * streams, or two threads) race and give undefined results; calls ordered on
+ * one stream are safe.  Arguments, outputs and the other errors as
+ * fp4nv_msedn_quantize. */
+FP4MX_API int fp4nv_msedn_quantize_noalloc(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                                           int axis, float clip_s, uint64_t seed, uint32_t gemm_id,
+                                           uint32_t rng_stream, uint8_t* codes, uint8_t* scales,
+                                           float* tensor_scale, float* eden_s, void* stream);
 
 /* Workspace bytes for fp4nv_linear_bwd. */
 FP4MX_API size_t fp4nv_linear_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k);

@@ -195,3 +195,15 @@ print(" ".join(str(v) for v in out))
     assert r.returncode == 0, r.stderr
     assert r.stdout.split() == ["-6", "-6", "-6", "-1"]
     assert binding.lib().fp4mx_status_string(-6) == b"device is not gfx950"
+
+
+def test_noalloc_rejects_inputs_beyond_its_scratch():
+    """fp4nv_msedn_quantize_noalloc checks its static scratch bound on the
+    host, after the argument checks and before touching a device."""
+    L = binding.lib()
+    keep, p = _buf()
+    f = lambda r, c, x=p: L.fp4nv_msedn_quantize_noalloc(x, r, c, c, 0, 6.0, 0, 1, 5, p, p, p, None, None)
+    assert f(16384, 8192 + 128) == -8          # one 128-chunk per row beyond 2^27 elements
+    assert f(32768, 8192) == -8
+    assert f(64, 128, None) == -1               # argument checks come first
+    assert L.fp4mx_status_string(-8).startswith(b"input needs more scratch")
