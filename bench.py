@@ -37,12 +37,14 @@ PEAK_FP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 MX_BYTES_PER_ELEM = 2 + 0.5 + 1 / 32   # bf16 in, 4-bit code + 1/32 scale byte out
+ROTATE_BYTES = 1 << 30                  # linear-layer inputs in rotation: at least 1 GiB
+DIST_STEPS = 200                        # steps timed one by one for the median
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", choices=["quartet", "llama"], default="quartet")
     p.add_argument("--no-extra", action="store_true", help="only the headline workload")
@@ -60,30 +62,49 @@ def dev_bf16(bits):
 class _Step:
     """A sequence of C-ABI launches on one stream, timed per step and per launch."""
 
+    def _step_calls(self):
+        """Launch lists, one per input set (step i uses set i % nsets)."""
+        return [self._calls(i) for i in range(getattr(self, "nsets", 1))]
+
     def run(self, steps, timed):
         """`steps` passes of the launches, back to back; when timed, one event
         before the first and one after the last launch (nothing is inserted
         between steps or kernels)."""
         import torch
-        calls = self._calls()
+        sc = self._step_calls()
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)] if timed else None
         if timed:
             evs[0].record()
-        for _ in range(steps):
-            for c in calls:
+        for i in range(steps):
+            for c in sc[i % len(sc)]:
                 c()
         if timed:
             evs[1].record()
         return evs
+
+    def step_times(self, steps):
+        """Duration of each of `steps` back-to-back steps: one event at every
+        step boundary (ms per step, a list)."""
+        import torch
+        sc = self._step_calls()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            for c in sc[i % len(sc)]:
+                c()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
     def kernel_times(self, steps):
         """In-step duration of each launch: the same steps again with an event
         after every launch, all on the stream the kernels run on (an event
         record adds a few microseconds to the launch it follows)."""
         import torch
-        calls = self._calls()
+        sc = self._step_calls()
         evs = []
-        for _ in range(steps):
+        for s_ in range(steps):
+            calls = sc[s_ % len(sc)]
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
             ev[0].record()
             for i, c in enumerate(calls):
@@ -102,11 +123,19 @@ class _Step:
 class LinearStep(_Step):
     """The MXFP4 linear fwd+bwd hot path as six C-ABI launches on one stream."""
 
-    def __init__(self, d, seed=0):
+    def __init__(self, d, seed=0, rotate_bytes=ROTATE_BYTES):
         import torch
         import fp4_microscaled_quantized_amd as fq
         self.fq = fq
-        self.x, self.w, self.dy = dev_bf16(d["x"]), dev_bf16(d["w"]), dev_bf16(d["dy"])
+        x, w, dy = dev_bf16(d["x"]), dev_bf16(d["w"]), dev_bf16(d["dy"])
+        # input sets in rotation: step i reads set i % nsets, and the sets
+        # together exceed the 256 MB Infinity Cache several times over, so a
+        # step's inputs come from HBM (copies hold the same values)
+        per_set = (x.numel() + w.numel() + dy.numel()) * 2
+        self.nsets = max(1, -(-rotate_bytes // per_set))
+        self.sets = [(x, w, dy)] + [(x.clone(), w.clone(), dy.clone()) for _ in range(self.nsets - 1)]
+        self.x, self.w, self.dy = x, w, dy
+        self.rotating_MB = round(self.nsets * per_set / 1e6, 1)
         self.m, self.k = self.x.shape
         self.n = self.w.shape[0]
         self.seed = seed
@@ -122,23 +151,24 @@ class LinearStep(_Step):
         self.names = ["quant_x", "quant_w", "gemm_y", "quant_dy", "gemm_dx", "gemm_dw"]
         self.times = {nm: [] for nm in self.names}
 
-    def _calls(self):
-        fq, L, C = self.fq, self.fq.lib(), None
+    def _calls(self, i=0):
+        fq, L = self.fq, self.fq.lib()
         from fp4_microscaled_quantized_amd.binding import _check, _ptr, _stream
         s = _stream()
         m, n, k, seed = self.m, self.n, self.k, self.seed
         g0, g1, g2 = self.g
         RTN, SR = fq.RTN, fq.SR
+        x, w, dy = self.sets[i % self.nsets]
         return [
-            lambda: _check(L.fp4mx_hadamard_quantize_dual(_ptr(self.x), m, k, k, RTN, g0, 0, SR, g2, 4, seed,
+            lambda: _check(L.fp4mx_hadamard_quantize_dual(_ptr(x), m, k, k, RTN, g0, 0, SR, g2, 4, seed,
                                                           _ptr(self.xq), _ptr(self.xs), _ptr(self.xtq),
                                                           _ptr(self.xts), s)),
-            lambda: _check(L.fp4mx_hadamard_quantize_dual(_ptr(self.w), n, k, k, RTN, g0, 0, SR, g1, 2, seed,
+            lambda: _check(L.fp4mx_hadamard_quantize_dual(_ptr(w), n, k, k, RTN, g0, 0, SR, g1, 2, seed,
                                                           _ptr(self.wq), _ptr(self.wsc), _ptr(self.wtq),
                                                           _ptr(self.wts), s)),
             lambda: _check(L.fp4mx_gemm(_ptr(self.xq), _ptr(self.xs), _ptr(self.wq), _ptr(self.wsc), m, n, k,
                                         1.0, _ptr(self.y), n, s)),
-            lambda: _check(L.fp4mx_hadamard_quantize_dual(_ptr(self.dy), m, n, n, SR, g1, 1, SR, g2, 3, seed,
+            lambda: _check(L.fp4mx_hadamard_quantize_dual(_ptr(dy), m, n, n, SR, g1, 1, SR, g2, 3, seed,
                                                           _ptr(self.dq), _ptr(self.ds), _ptr(self.dtq),
                                                           _ptr(self.dts), s)),
             lambda: _check(L.fp4mx_gemm(_ptr(self.dq), _ptr(self.ds), _ptr(self.wtq), _ptr(self.wts), m, k, n,
@@ -189,7 +219,7 @@ class QuestStep(_Step):
                       "gemm_dx_irht", "gemm_dw_irht"]
         self.times = {nm: [] for nm in self.names}
 
-    def _calls(self):
+    def _calls(self, i=0):
         fq, L = self.fq, self.fq.lib()
         from fp4_microscaled_quantized_amd.binding import _check, _ptr, _stream
         s = _stream()
@@ -233,9 +263,14 @@ class QuestStep(_Step):
             raise SystemExit("decomposed QuEST step differs from fp4mx_quest_linear_fwd/bwd")
 
 
-def time_step(st, steps, warmup):
+def time_step(st, steps, warmup, dist_steps=0):
+    """Optionally `dist_steps` steps with an event at every step boundary (the
+    distribution; they also bring the clocks to their steady state), then
+    the warm-up, then `steps` timed steps (wall clock and one event pair),
+    then the per-kernel pass."""
     import torch
     st.check_against_composite()
+    dist = st.step_times(dist_steps) if dist_steps else None
     st.run(warmup, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -245,7 +280,7 @@ def time_step(st, steps, warmup):
     step_ms = [evs[0].elapsed_time(evs[1]) / steps]
     st.kernel_times(steps)
     avg = {nm: float(np.mean(v)) for nm, v in st.times.items()}
-    return wall, avg, step_ms
+    return wall, avg, step_ms, dist
 
 
 def time_quest(steps, warmup):
@@ -254,7 +289,7 @@ def time_quest(steps, warmup):
     element, re-quantizer 2 x 0.53125)."""
     from fp4_microscaled_quantized_amd import synth
     st = QuestStep(synth.quartet_linear(0))
-    wall, avg, _ = time_step(st, steps, warmup)
+    wall, avg, _, _ = time_step(st, steps, warmup)
     ms = wall * 1e3 / steps
     m, n, k = st.m, st.n, st.k
     by = {"quest_x": m * k * (2 + 0.5 + 1 / 32 + 1 / 8), "quest_w": n * k * (2 + 0.5 + 1 / 32 + 1 / 8),
@@ -269,10 +304,10 @@ def time_quest(steps, warmup):
             "breakdown_ms": {nm: round(v, 4) for nm, v in avg.items()}, "kernel_hbm": kr}
 
 
-def time_linear(d, steps, warmup, seed=0):
+def time_linear(d, steps, warmup, seed=0, dist_steps=0):
     st = LinearStep(d, seed)
-    wall, avg, step_ms = time_step(st, steps, warmup)
-    return st, wall, avg, step_ms
+    wall, avg, step_ms, dist = time_step(st, steps, warmup, dist_steps)
+    return st, wall, avg, step_ms, dist
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "mx_gemm_kernel_quartet_8192x4096x4096_traffic.json")
@@ -582,23 +617,48 @@ def time_quartet2(steps, warmup):
     return res
 
 
-def cpu_baseline(rows=1024, target_s=25.0):
-    """The oracle's linear fwd+bwd on the first `rows` tokens of the headline
-    workload.  If that takes under 10 s on this host, the sample grows once,
-    in whole 32-row blocks (at most the full 8192 rows), by target_s / time:
-    the per-row cost falls as the fixed weight work is amortised, so the
-    second run lands in the 10-30 s range rather than at target_s."""
-    from fp4_microscaled_quantized_amd import synth
+def _oracle_quant_rows(args):
+    """Worker: the oracle's MXFP4 quantizer on a chunk of rows (spawned process)."""
     from oracle import mx
+    x, kw, row_ids = args
+    return mx.quantize(x, row_ids=row_ids, **kw)
+
+
+def _cpu_model():
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(rows=1024, target_s=12.0):
+    """The oracle on the host's cores.
+
+    value: the oracle's linear fwd+bwd on the first `rows` tokens of the
+    headline workload (TFLOP/s).  If that takes under 8 s the sample grows
+    once, in whole 32-row blocks, by target_s / time (the fixed weight work is
+    amortised, so the second run lands near target_s).  NumPy's elementwise
+    work runs on one thread, its fp64 matmuls on all BLAS threads.
+
+    full_size: the 8192 x 4096 quantizer (RHT + RTN, 84.9 MB of algorithmic
+    traffic) and the 8192 x 4096 x 4096 GEMM (on operands quantized
+    beforehand), each at full size, on 1 thread and on all cores (row chunks
+    over worker processes for the quantizer, BLAS threads for the GEMM)."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from fp4_microscaled_quantized_amd import synth
+    from oracle import mx, rng
     d = synth.quartet_linear(0)
     f = synth.bf16_bits_to_f32
     w = f(d["w"])
     n, k = w.shape
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas = 1
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    workers = max(1, min(16, os.cpu_count() or 1))
 
     def run(r):
         x, dy = f(d["x"][:r]), f(d["dy"][:r])
@@ -608,14 +668,56 @@ def cpu_baseline(rows=1024, target_s=25.0):
         return time.perf_counter() - t0
 
     dt = run(rows)
-    if dt < 10.0:
+    if dt < 8.0:
         rows = min(8192, max(rows, int(rows * target_s / dt) // 32 * 32))
         dt = run(rows)
     flop = 6.0 * rows * n * k
-    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
-            "sample": "linear fwd+bwd on the first %d of 8192 token rows of the 8192x4096x4096 workload "
-                      "(6*%d*4096*4096 flop) in %.1f s; numpy elementwise on 1 thread, fp64 matmul on %d "
-                      "BLAS threads" % (rows, rows, dt, blas)}
+    res = {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
+           "sample": "linear fwd+bwd on the first %d of 8192 token rows of the 8192x4096x4096 workload "
+                     "(6*%d*4096*4096 flop) in %.1f s; numpy elementwise on 1 thread, fp64 matmul on %d "
+                     "BLAS threads" % (rows, rows, dt, blas),
+           "cpu_model": _cpu_model(), "host_cpus_visible": os.cpu_count()}
+
+    # full-size quantizer: 8192 x 4096, RHT + RTN (GEMM-0 mask)
+    xq = f(synth.quantizer_tensor()["x"])
+    R, Cq = xq.shape
+    kw = dict(rounding=mx.RTN, sign_mask=rng.sign_mask(0, 0))
+    qbytes = R * Cq * (2 + 0.5 + 1 / 32)
+    t0 = time.perf_counter()
+    mx.quantize(xq, **kw)
+    q1 = time.perf_counter() - t0
+    bounds = np.linspace(0, R, 4 * workers + 1).astype(int)
+    tasks = [(xq[a:b], kw, np.arange(a, b)) for a, b in zip(bounds[:-1], bounds[1:])]
+    with mp.get_context("spawn").Pool(workers) as pool:
+        pool.map(_oracle_quant_rows, tasks[:workers])           # start the workers
+        t0 = time.perf_counter()
+        pool.map(_oracle_quant_rows, tasks)
+        qn = time.perf_counter() - t0
+        # GEMM operands for the full-size GEMM, quantized in the same pool (untimed)
+        x, g0 = f(d["x"]), rng.sign_mask(0, 0)
+        gkw = dict(rounding=mx.RTN, sign_mask=g0)
+        parts = []
+        for src in (x, w):
+            b2 = np.linspace(0, src.shape[0], 4 * workers + 1).astype(int)
+            ps = pool.map(_oracle_quant_rows, [(src[a:b], gkw, np.arange(a, b)) for a, b in zip(b2[:-1], b2[1:])])
+            parts.append((np.concatenate([p[0] for p in ps]), np.concatenate([p[1] for p in ps])))
+    gflop = 2.0 * x.shape[0] * n * k
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        mx.gemm(*parts[0], *parts[1])
+        g1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    mx.gemm(*parts[0], *parts[1])
+    gn = time.perf_counter() - t0
+    res["full_size"] = {
+        "quantizer_8192x4096_rht_rtn": {
+            "1_thread": {"s": round(q1, 2), "GB/s": round(qbytes / q1 / 1e9, 4)},
+            "all_cores": {"s": round(qn, 2), "GB/s": round(qbytes / qn / 1e9, 4), "processes": workers}},
+        "gemm_8192x4096x4096": {
+            "1_thread": {"s": round(g1, 2), "TFLOP/s": round(gflop / g1 / 1e12, 5)},
+            "all_cores": {"s": round(gn, 2), "TFLOP/s": round(gflop / gn / 1e12, 5), "blas_threads": int(blas)},
+            "note": "dequantize to fp64 and one fp64 matmul (the oracle's GEMM)"}}
+    return res
 
 
 def main():
@@ -643,21 +745,29 @@ def main():
     else:
         d = synth.llama_ffn_up(0)
         wl = {"workload": "llama3_8b_ffn_up fwd+bwd M=8192 K=4096 N=14336", "m": 8192, "n": 14336, "k": 4096}
-    st, wall, avg, step_ms = time_linear(d, a.steps, a.warmup)
+    st, wall, avg, step_ms, dist = time_linear(d, a.steps, a.warmup, dist_steps=max(a.steps, DIST_STEPS))
     ev_ms = sum(avg.values())
     ms_step = wall * 1e3 / a.steps
     value = st.flops() / (ms_step * 1e-3) / 1e12
+    med = float(np.median(dist))
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
-        "data": "synthetic", "config": {**wl, "seed": 0, "parallelism": "none (1 GPU)"},
+        "data": "synthetic", "config": {**wl, "seed": 0, "parallelism": "none (1 GPU)",
+                                        "rotating_input_sets": st.nsets, "rotating_inputs_MB": st.rotating_MB},
         "frac_fp4_peak": round(value / PEAK_FP4_TFLOPS, 4),
         "roofline": gemm_roofline(st, avg),
         "mfma_fp4_sustained": mfma_sustained(4),
         "breakdown_ms": {k2: round(v, 4) for k2, v in avg.items()},
         "kernel_sum_ms_per_step": round(ev_ms, 4),
         "event_ms_per_step": round(float(np.mean(step_ms)), 4),
+        "step_distribution": {"steps": len(dist), "median_ms": round(med, 4),
+                              "mean_ms": round(float(np.mean(dist)), 4),
+                              "p10_ms": round(float(np.percentile(dist, 10)), 4),
+                              "p90_ms": round(float(np.percentile(dist, 90)), 4),
+                              "median_TFLOP/s": round(st.flops() / (med * 1e-3) / 1e12, 1),
+                              "note": "one event at every step boundary, inputs rotating over the sets above"},
         "quantizer_roofline_in_step": quant_roofline(st, avg),
     }
     sus = out["mfma_fp4_sustained"]["random_operands"]["TFLOP/s"]
@@ -667,7 +777,7 @@ def main():
     torch.cuda.empty_cache()
     if not a.no_extra:
         if a.workload == "quartet":
-            st2, wall2, avg2, _ = time_linear(synth.llama_ffn_up(0), a.steps, a.warmup)
+            st2, wall2, avg2, _, _ = time_linear(synth.llama_ffn_up(0), a.steps, a.warmup)
             ms2 = wall2 * 1e3 / a.steps
             out["llama_ffn_up"] = {"workload": "8192 x 4096 -> 14336 fwd+bwd", "ms_per_step": round(ms2, 4),
                                    "TFLOP/s": round(st2.flops() / (ms2 * 1e-3) / 1e12, 1),

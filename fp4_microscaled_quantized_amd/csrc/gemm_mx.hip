@@ -149,6 +149,141 @@ __device__ __forceinline__ void tile_of(int wg, int gm, int gn, int& tm, int& tn
   tn = r / gsz;
 }
 
+// ---- epilogue: lane l, reg v -> row 8(v/4) + 4(l/32) + v%4, col l%32 ----
+// Shared by both main loops.  The LDS stage buffers are free when it runs.
+template <int EPI, int WM, int WN>
+__device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[kBM / WM / 32][kBN / WN / 32], uint8_t* lds,
+                                              int lane, int wave, int m0, int n0, int M, int N,
+                                              int ldc, float alpha, float* __restrict__ C,
+                                              const uint32_t* __restrict__ cmask,
+                                              uint32_t sign_mask) {
+  constexpr int FM = kBM / WM / 32, FN = kBN / WN / 32;
+  const int wm = wave / WN, wn = wave % WN;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int rowsC = min(kBM, M - m0);
+  constexpr uint32_t kCB = EPI == kEpiBf16 ? 2u : 4u;  // bytes per C element
+  const rsrc_t rC = make_rsrc(reinterpret_cast<uint8_t*>(C) + (size_t)m0 * ldc * kCB,
+                              (uint32_t)rowsC * (uint32_t)ldc * kCB);
+  if constexpr (EPI == kEpiF32) {
+    // straight from the accumulators: per instruction two 128-B row pieces
+    // (measured faster here than staging through LDS for whole-row stores)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * (kBN / WN) + j * 32 + fr;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * (kBM / WM) + i * 32 + 8 * (v / 4) + 4 * fh + (v % 4);
+          const uint32_t bad = 0u - (uint32_t)(col >= N);
+          const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 4u) & ~bad) | (kOOB & bad);
+          buf_store4(alpha * acc[i][j][v], rC, off);
+        }
+      }
+    }
+  } else {
+    // The stage buffers are free after the last barrier: each wave stages
+    // one 32-row block of its sub-tile at a time (32 x 128 fp32, row pitch
+    // 132 floats) and stores it row by row with 16-B stores.
+    // IRHT: before the store every lane takes two whole 32-column groups of
+    // the block and replaces each by H^-1((alpha acc) with masked entries
+    // zeroed), H^-1 y = s o (c FWHT(y)) (a lane storing its own group would
+    // touch 64 cache lines per instruction).  BF16: the store pass rounds
+    // eight consecutive values per lane to bf16.
+    static_assert(WM * WN * 32 * 132 * 4 <= 2 * kStageLds, "epilogue staging exceeds LDS");
+    static_assert(FN * 32 == 128 && kBN / WN == 128, "the store pass assumes 128-column wave sub-tiles");
+    float* stg = reinterpret_cast<float*>(lds) + wave * (32 * 132);
+    const int gpr = N / 32;  // mask words per row
+    const rsrc_t rM = make_rsrc(EPI == kEpiIrht ? cmask + (size_t)m0 * gpr : nullptr,
+                                EPI == kEpiIrht ? (uint32_t)rowsC * (uint32_t)gpr * 4u : 0u);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          stg[(8 * (v / 4) + 4 * fh + (v % 4)) * 132 + 32 * j + fr] = alpha * acc[i][j][v];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+      __builtin_amdgcn_wave_barrier();
+      if constexpr (EPI == kEpiIrht) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int item = lane + 64 * u;             // 32 rows x 4 groups
+          const int rl = item >> 2, gq = item & 3;
+          float t[32];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float4 w = *reinterpret_cast<const float4*>(stg + rl * 132 + 32 * gq + 4 * q);
+            t[4 * q] = w.x; t[4 * q + 1] = w.y; t[4 * q + 2] = w.z; t[4 * q + 3] = w.w;
+          }
+          const int col0 = n0 + wn * (kBN / WN) + 32 * gq;     // first column of the group
+          const uint32_t badc = 0u - (uint32_t)(col0 >= N);
+          const int row = wm * (kBM / WM) + i * 32 + rl;       // within the tile
+          const uint32_t moff = ((((uint32_t)row * (uint32_t)gpr + (uint32_t)(col0 >> 5)) * 4u) & ~badc) | (kOOB & badc);
+          const uint32_t mb = buf_load4(rM, moff);
+#pragma unroll
+          for (int e = 0; e < 32; ++e) t[e] = ((mb >> e) & 1u) ? 0.0f : t[e];
+#pragma unroll
+          for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+              if (e & h) continue;
+              const float a = t[e], b = t[e + h];
+              t[e] = a + b;
+              t[e + h] = a - b;
+            }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int k = 4 * q + e;
+              const float y = t[k] * 0x1.6a09e6p-3f;  // fl32(1/sqrt(32))
+              o[e] = __uint_as_float(__float_as_uint(y) ^ (((sign_mask >> k) & 1u) << 31));
+            }
+            *reinterpret_cast<float4*>(stg + rl * 132 + 32 * gq + 4 * q) = float4{o[0], o[1], o[2], o[3]};
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // the transformed block is in LDS
+        __builtin_amdgcn_wave_barrier();
+      }
+      if constexpr (EPI == kEpiIrht) {
+        // row-contiguous stores: one instruction covers two 128-column rows
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int f = 64 * k + lane, rl = f >> 5, c4 = f & 31;
+          const float4 w = *reinterpret_cast<const float4*>(stg + rl * 132 + 4 * c4);
+          const int row = wm * (kBM / WM) + i * 32 + rl;
+          const int col = n0 + wn * (kBN / WN) + 4 * c4;
+          const uint32_t bad = 0u - (uint32_t)(col >= N);
+          const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 4u) & ~bad) | (kOOB & bad);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, w), rC, (int)off, 0, kStoreNT);
+        }
+      } else {
+        // bf16: eight consecutive columns per lane, one instruction covers
+        // four 128-column rows
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int f = 64 * k + lane, rl = f >> 4, c8 = f & 15;
+          const float4 w0 = *reinterpret_cast<const float4*>(stg + rl * 132 + 8 * c8);
+          const float4 w1 = *reinterpret_cast<const float4*>(stg + rl * 132 + 8 * c8 + 4);
+          const int row = wm * (kBM / WM) + i * 32 + rl;
+          const int col = n0 + wn * (kBN / WN) + 8 * c8;
+          const uint32_t bad = 0u - (uint32_t)(col >= N);
+          const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 2u) & ~bad) | (kOOB & bad);
+          const __attribute__((ext_vector_type(4))) unsigned int o = {
+              bf16_rne(w0.x) | (bf16_rne(w0.y) << 16), bf16_rne(w0.z) | (bf16_rne(w0.w) << 16),
+              bf16_rne(w1.x) | (bf16_rne(w1.y) << 16), bf16_rne(w1.z) | (bf16_rne(w1.w) << 16)};
+          __builtin_amdgcn_raw_buffer_store_b128(o, rC, (int)off, 0, kStoreNT);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // this block's reads are done before it is overwritten
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 template <int FMT, bool VEC, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
@@ -377,129 +512,7 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
     __syncthreads();
   }
 
-  // ---- epilogue: lane l, reg v -> row 8(v/4) + 4(l/32) + v%4, col l%32 ----
-  const int rowsC = min(kBM, M - m0);
-  constexpr uint32_t kCB = EPI == kEpiBf16 ? 2u : 4u;  // bytes per C element
-  const rsrc_t rC = make_rsrc(reinterpret_cast<uint8_t*>(C) + (size_t)m0 * ldc * kCB,
-                              (uint32_t)rowsC * (uint32_t)ldc * kCB);
-  if constexpr (EPI == kEpiF32) {
-    // straight from the accumulators: per instruction two 128-B row pieces
-    // (measured faster here than staging through LDS for whole-row stores)
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * (kBN / WN) + j * 32 + fr;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = wm * (kBM / WM) + i * 32 + 8 * (v / 4) + 4 * fh + (v % 4);
-          const uint32_t bad = 0u - (uint32_t)(col >= N);
-          const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 4u) & ~bad) | (kOOB & bad);
-          buf_store4(alpha * acc[i][j][v], rC, off);
-        }
-      }
-    }
-  } else {
-    // The stage buffers are free after the last barrier: each wave stages
-    // one 32-row block of its sub-tile at a time (32 x 128 fp32, row pitch
-    // 132 floats) and stores it row by row with 16-B stores.
-    // IRHT: before the store every lane takes two whole 32-column groups of
-    // the block and replaces each by H^-1((alpha acc) with masked entries
-    // zeroed), H^-1 y = s o (c FWHT(y)) (a lane storing its own group would
-    // touch 64 cache lines per instruction).  BF16: the store pass rounds
-    // eight consecutive values per lane to bf16.
-    static_assert(WM * WN * 32 * 132 * 4 <= 2 * kStageLds, "epilogue staging exceeds LDS");
-    static_assert(FN * 32 == 128 && kBN / WN == 128, "the store pass assumes 128-column wave sub-tiles");
-    float* stg = reinterpret_cast<float*>(lds) + wave * (32 * 132);
-    const int gpr = N / 32;  // mask words per row
-    const rsrc_t rM = make_rsrc(EPI == kEpiIrht ? cmask + (size_t)m0 * gpr : nullptr,
-                                EPI == kEpiIrht ? (uint32_t)rowsC * (uint32_t)gpr * 4u : 0u);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          stg[(8 * (v / 4) + 4 * fh + (v % 4)) * 132 + 32 * j + fr] = alpha * acc[i][j][v];
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
-      __builtin_amdgcn_wave_barrier();
-      if constexpr (EPI == kEpiIrht) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int item = lane + 64 * u;             // 32 rows x 4 groups
-          const int rl = item >> 2, gq = item & 3;
-          float t[32];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float4 w = *reinterpret_cast<const float4*>(stg + rl * 132 + 32 * gq + 4 * q);
-            t[4 * q] = w.x; t[4 * q + 1] = w.y; t[4 * q + 2] = w.z; t[4 * q + 3] = w.w;
-          }
-          const int col0 = n0 + wn * (kBN / WN) + 32 * gq;     // first column of the group
-          const uint32_t badc = 0u - (uint32_t)(col0 >= N);
-          const int row = wm * (kBM / WM) + i * 32 + rl;       // within the tile
-          const uint32_t moff = ((((uint32_t)row * (uint32_t)gpr + (uint32_t)(col0 >> 5)) * 4u) & ~badc) | (kOOB & badc);
-          const uint32_t mb = buf_load4(rM, moff);
-#pragma unroll
-          for (int e = 0; e < 32; ++e) t[e] = ((mb >> e) & 1u) ? 0.0f : t[e];
-#pragma unroll
-          for (int h = 1; h < 32; h <<= 1)
-#pragma unroll
-            for (int e = 0; e < 32; ++e) {
-              if (e & h) continue;
-              const float a = t[e], b = t[e + h];
-              t[e] = a + b;
-              t[e + h] = a - b;
-            }
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int k = 4 * q + e;
-              const float y = t[k] * 0x1.6a09e6p-3f;  // fl32(1/sqrt(32))
-              o[e] = __uint_as_float(__float_as_uint(y) ^ (((sign_mask >> k) & 1u) << 31));
-            }
-            *reinterpret_cast<float4*>(stg + rl * 132 + 32 * gq + 4 * q) = float4{o[0], o[1], o[2], o[3]};
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // the transformed block is in LDS
-        __builtin_amdgcn_wave_barrier();
-      }
-      if constexpr (EPI == kEpiIrht) {
-        // row-contiguous stores: one instruction covers two 128-column rows
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int f = 64 * k + lane, rl = f >> 5, c4 = f & 31;
-          const float4 w = *reinterpret_cast<const float4*>(stg + rl * 132 + 4 * c4);
-          const int row = wm * (kBM / WM) + i * 32 + rl;
-          const int col = n0 + wn * (kBN / WN) + 4 * c4;
-          const uint32_t bad = 0u - (uint32_t)(col >= N);
-          const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 4u) & ~bad) | (kOOB & bad);
-          __builtin_amdgcn_raw_buffer_store_b128(
-              __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, w), rC, (int)off, 0, kStoreNT);
-        }
-      } else {
-        // bf16: eight consecutive columns per lane, one instruction covers
-        // four 128-column rows
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int f = 64 * k + lane, rl = f >> 4, c8 = f & 15;
-          const float4 w0 = *reinterpret_cast<const float4*>(stg + rl * 132 + 8 * c8);
-          const float4 w1 = *reinterpret_cast<const float4*>(stg + rl * 132 + 8 * c8 + 4);
-          const int row = wm * (kBM / WM) + i * 32 + rl;
-          const int col = n0 + wn * (kBN / WN) + 8 * c8;
-          const uint32_t bad = 0u - (uint32_t)(col >= N);
-          const uint32_t off = ((((uint32_t)row * (uint32_t)ldc + (uint32_t)col) * 2u) & ~bad) | (kOOB & bad);
-          const __attribute__((ext_vector_type(4))) unsigned int o = {
-              bf16_rne(w0.x) | (bf16_rne(w0.y) << 16), bf16_rne(w0.z) | (bf16_rne(w0.w) << 16),
-              bf16_rne(w1.x) | (bf16_rne(w1.y) << 16), bf16_rne(w1.z) | (bf16_rne(w1.w) << 16)};
-          __builtin_amdgcn_raw_buffer_store_b128(o, rC, (int)off, 0, kStoreNT);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // this block's reads are done before it is overwritten
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
+  gemm_epilogue<EPI, WM, WN>(acc, lds, lane, wave, m0, n0, M, N, ldc, alpha, C, cmask, sign_mask);
 }
 
 template <int FMT, bool VEC, int WM, int WN, int EPI>
