@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--workload", choices=["quartet", "llama"], default="quartet")
     p.add_argument("--no-extra", action="store_true", help="only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--dist-steps", type=int, default=DIST_STEPS,
+                   help="steps timed one by one for the step-time distribution (0: none)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one 512 MiB device copy (traffic counter calibration)")
     return p.parse_args()
@@ -636,14 +638,15 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(rows=1024, target_s=12.0):
+def cpu_baseline(rows=1024, target_s=15.0):
     """The oracle on the host's cores.
 
     value: the oracle's linear fwd+bwd on the first `rows` tokens of the
-    headline workload (TFLOP/s).  If that takes under 8 s the sample grows
-    once, in whole 32-row blocks, by target_s / time (the fixed weight work is
-    amortised, so the second run lands near target_s).  NumPy's elementwise
-    work runs on one thread, its fp64 matmuls on all BLAS threads.
+    headline workload (TFLOP/s).  The time is a fixed part (the weight's
+    quantizations) plus a part per row; a 32-row run and a `rows`-row run fit
+    the two, and the sample is then sized, in whole 32-row blocks, so that the
+    timed run takes about target_s.  NumPy's elementwise work runs on one
+    thread, its fp64 matmuls on all BLAS threads.
 
     full_size: the 8192 x 4096 quantizer (RHT + RTN, 84.9 MB of algorithmic
     traffic) and the 8192 x 4096 x 4096 GEMM (on operands quantized
@@ -667,9 +670,12 @@ def cpu_baseline(rows=1024, target_s=12.0):
         mx.linear_bwd(dy, ctx)
         return time.perf_counter() - t0
 
+    t_fix = run(32)
     dt = run(rows)
-    if dt < 8.0:
-        rows = min(8192, max(rows, int(rows * target_s / dt) // 32 * 32))
+    per_row = max(dt - t_fix, 1e-3) / (rows - 32)
+    grown = int((target_s - t_fix) / per_row) // 32 * 32
+    if grown > rows:
+        rows = min(8192, grown)
         dt = run(rows)
     flop = 6.0 * rows * n * k
     res = {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
@@ -745,10 +751,12 @@ def main():
     else:
         d = synth.llama_ffn_up(0)
         wl = {"workload": "llama3_8b_ffn_up fwd+bwd M=8192 K=4096 N=14336", "m": 8192, "n": 14336, "k": 4096}
-    st, wall, avg, step_ms, dist = time_linear(d, a.steps, a.warmup, dist_steps=max(a.steps, DIST_STEPS))
+    st, wall, avg, step_ms, dist = time_linear(d, a.steps, a.warmup,
+                                              dist_steps=max(a.steps, a.dist_steps) if a.dist_steps else 0)
     ev_ms = sum(avg.values())
     ms_step = wall * 1e3 / a.steps
     value = st.flops() / (ms_step * 1e-3) / 1e12
+    dist = dist if dist else step_ms
     med = float(np.median(dist))
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1,

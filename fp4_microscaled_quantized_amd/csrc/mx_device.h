@@ -73,9 +73,9 @@ __device__ __forceinline__ uint32_t sr_bits(uint32_t h1, int i) {
 // pair (a, b) into byte B of its destination and keeps the other bytes.  It
 // truncates an element's position inside its E2M1 gap to 22 bits, adds the
 // top 22 bits of the seed (of the seed shifted left by one for b) and keeps
-// the carry; the sign is the sign of the input.  Seeded with r for a and
-// r >> 1 for b, both elements round up iff floor(p * 2^22) + (r >> 10) >=
-// 2^22, p being the position in the gap.  The compiler's builtin for this
+// the carry; the sign is the sign of the input.  Seeded with r, element a
+// rounds up iff floor(p * 2^22) + (r >> 10) >= 2^22, p being the position in
+// the gap, and +0 in slot b gives nibble 0.  The compiler's builtin for this
 // instruction does not keep the destination's other bytes, hence the asm
 // with a read-write operand.
 template <int B>
@@ -95,13 +95,16 @@ __device__ __forceinline__ void cvt_sr_fp4(uint32_t& acc, float a, float b, uint
         : "+v"(acc) : "v"(v), "v"(seed));
 }
 
-// SR of the element pair (v0, v1) with draws r0, r1 into byte B: v0's nibble
-// lands in `lo` (low nibble), v1's in `hi` (high nibble).
+// SR of the element pair (v0, v1) with draws r0, r1 into byte B: each
+// element is converted on its own in slot a (the slot that reads its draw
+// as is), v0's nibble into the low nibble of byte B of `lo`, v1's into the
+// low nibble of byte B of `hi`; the caller moves `hi` up by four bits.  One
+// seed per pair would hand the two elements draws sharing 21 of 22 bits.
 template <int B>
 __device__ __forceinline__ void sr_pair(uint32_t& lo, uint32_t& hi, float v0, float v1,
                                         uint32_t r0, uint32_t r1) {
   cvt_sr_fp4<B>(lo, v0, 0.0f, r0);
-  cvt_sr_fp4<B>(hi, 0.0f, v1, r1 >> 1);
+  cvt_sr_fp4<B>(hi, v1, 0.0f, r1);
 }
 
 // Quantize one group held in registers.  Writes 4 code words (8 nibbles
@@ -153,9 +156,14 @@ __device__ __forceinline__ void quant_group(const float (&y)[kGroup], uint32_t i
     const uint32_t h1 = h0 ^ (h0 >> 16);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      // Even elements go to byte b of `lo`, odd ones to byte b of `hi`; the
-      // other element of each converted pair is +0, which gives nibble 0.
-      uint32_t lo = 0, hi = 0;
+      // Even elements go to the low nibble of byte b of `lo`, odd ones to
+      // the low nibble of byte b of `hi` (shifted into the high nibble
+      // below); the other element of each converted pair is +0, nibble 0.
+      // The four conversions write every byte of lo and hi, so their
+      // starting contents do not matter: an empty asm defines them without
+      // an instruction.
+      uint32_t lo, hi;
+      asm volatile("" : "=v"(lo), "=v"(hi));
       sr_pair<0>(lo, hi, y[8 * k + 0] * f, y[8 * k + 1] * f, sr_bits(h1, 8 * k + 0),
                  sr_bits(h1, 8 * k + 1));
       sr_pair<1>(lo, hi, y[8 * k + 2] * f, y[8 * k + 3] * f, sr_bits(h1, 8 * k + 2),
@@ -164,7 +172,7 @@ __device__ __forceinline__ void quant_group(const float (&y)[kGroup], uint32_t i
                  sr_bits(h1, 8 * k + 5));
       sr_pair<3>(lo, hi, y[8 * k + 6] * f, y[8 * k + 7] * f, sr_bits(h1, 8 * k + 6),
                  sr_bits(h1, 8 * k + 7));
-      w[k] = lo | hi;
+      w[k] = lo | (hi << 4);
     }
   }
 }
