@@ -41,6 +41,14 @@ ROTATE_BYTES = 1 << 30                  # linear-layer inputs in rotation: at le
 DIST_STEPS = 200                        # steps timed one by one for the median
 
 
+_T0 = time.time()
+
+
+def progress(msg):
+    """One progress line on stderr (stdout carries only the JSON result)."""
+    print("[bench %6.1f s] %s" % (time.time() - _T0, msg), file=sys.stderr, flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -51,6 +59,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--dist-steps", type=int, default=DIST_STEPS,
                    help="steps timed one by one for the step-time distribution (0: none)")
+    p.add_argument("--vendor", action="store_true",
+                   help="also time hipBLASLt's MXFP4 GEMM beside the kernel (its set-up takes minutes)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one 512 MiB device copy (traffic counter calibration)")
     return p.parse_args()
@@ -97,6 +107,24 @@ class _Step:
             ev[i + 1].record()
         torch.cuda.synchronize()
         return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+    def group_time(self, idx, steps, warmup):
+        """Mean time of one pass over the launches idx of the step (the
+        step's own calls and buffers), `steps` passes back to back between
+        one event pair after `warmup` untimed passes: ms per pass."""
+        import torch
+        sc = self._step_calls()
+        for i in range(warmup):
+            for j in idx:
+                sc[i % len(sc)][j]()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for i in range(steps):
+            for j in idx:
+                sc[i % len(sc)][j]()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps
 
     def kernel_times(self, steps):
         """In-step duration of each launch: the same steps again with an event
@@ -309,6 +337,8 @@ def time_quest(steps, warmup):
 def time_linear(d, steps, warmup, seed=0, dist_steps=0):
     st = LinearStep(d, seed)
     wall, avg, step_ms, dist = time_step(st, steps, warmup, dist_steps)
+    # the three GEMMs of the step back to back (no event between launches)
+    st.gemm_pass_ms = st.group_time([2, 4, 5], steps, warmup)
     return st, wall, avg, step_ms, dist
 
 
@@ -334,11 +364,14 @@ def gemm_traffic(st):
 
 
 def gemm_roofline(st, avg):
-    """FP4 MFMA roofline of the GEMM kernel: 2MNK flop per launch / mean launch time."""
+    """FP4 MFMA roofline of the GEMM kernel: 2MNK flop per launch / mean launch
+    time, the time from the step's three GEMMs run back to back between one
+    event pair (an event after every launch, as in `avg`, adds a few
+    microseconds to each)."""
     m, n, k = st.m, st.n, st.k
     fl = {"gemm_y": 2.0 * m * n * k, "gemm_dx": 2.0 * m * k * n, "gemm_dw": 2.0 * n * k * m}
     tot_fl = sum(fl.values())
-    tot_ms = sum(avg[x] for x in fl)
+    tot_ms = st.gemm_pass_ms
     achieved = tot_fl / (tot_ms * 1e-3) / 1e12
     return {"bound": "mfma", "kernel": "mx_gemm_kernel (FP4 32x32x64 scaled MFMA)",
             "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
@@ -347,7 +380,10 @@ def gemm_roofline(st, avg):
             "algorithmic_bytes_per_launch": int(round(np.mean(
                 [(m + n) * k * 17 // 32 + 4 * m * n, (m + k) * n * 17 // 32 + 4 * m * k,
                  (n + k) * m * 17 // 32 + 4 * n * k]))),
-            "per_launch_ms": {x: round(avg[x], 4) for x in fl}}
+            "mean_launch_ms": round(tot_ms / 3, 4),
+            "mean_launch_timing": "the three GEMMs of the step, K passes back to back, one event pair",
+            "per_launch_ms": {x: round(avg[x], 4) for x in fl},
+            "per_launch_timing": "in the step, an event after every launch"}
 
 
 def mfma_sustained(fmt=4, iters=20000, reps=3):
@@ -525,6 +561,88 @@ def time_gemm_outputs(steps, warmup, rounds=3):
     return res
 
 
+def _vendor_lib():
+    import ctypes as C
+    from fp4_microscaled_quantized_amd import binding
+    L = C.CDLL(os.path.join(os.path.dirname(binding.LIB_PATH), "libfp4mx_vendor.so"))
+    L.fp4mx_vendor_plan_create.restype = C.c_int
+    L.fp4mx_vendor_plan_create.argtypes = [C.c_int64] * 3 + [C.POINTER(C.c_void_p), C.POINTER(C.c_int)]
+    L.fp4mx_vendor_gemm.restype = C.c_int
+    L.fp4mx_vendor_gemm.argtypes = [C.c_void_p, C.c_int] + [C.c_void_p] * 4 + [C.c_float, C.c_void_p, C.c_void_p]
+    L.fp4mx_vendor_plan_destroy.restype = None
+    L.fp4mx_vendor_plan_destroy.argtypes = [C.c_void_p]
+    return L
+
+
+def time_vendor_gemm(steps, warmup, rounds=3):
+    """hipBLASLt's MXFP4 GEMM (libfp4mx_vendor.so) beside fp4mx_gemm on the
+    same random operands and the same stream: the fastest of the heuristic
+    algorithms hipBLASLt offers (each timed over `steps` calls), then the two
+    timed alternately `rounds` times; medians.  The outputs' relative
+    Frobenius difference is reported as a sanity check."""
+    import ctypes as C
+    import torch
+    import fp4_microscaled_quantized_amd as fq
+    from fp4_microscaled_quantized_amd.binding import _stream
+    try:
+        V = _vendor_lib()
+    except OSError as e:
+        return {"unavailable": str(e)}
+    res = {"workload": "MXFP4 GEMM per launch, fp32 output, random codes and E8M0 scales 2^-9..2^3; "
+                       "hipBLASLt: VEC32_UE8M0 block scales, fastest of its heuristic algorithms"}
+    for (m, n, k) in [(8192, 4096, 4096), (8192, 14336, 4096)]:
+        key = "%dx%dx%d" % (m, n, k)
+        plan, nalg = C.c_void_p(), C.c_int()
+        st = V.fp4mx_vendor_plan_create(m, n, k, C.byref(plan), C.byref(nalg))
+        progress("  hipBLASLt plan %s: status %d, %d algorithms" % (key, st, nalg.value))
+        if st != 0:
+            res[key] = {"unavailable": "no hipBLASLt MXFP4 algorithm (status %d)" % st}
+            continue
+        try:
+            g = torch.Generator(device="cuda").manual_seed(11)
+
+            def padded(rows, cols, lo, hi):
+                t = torch.randint(lo, hi, (rows * cols + (1 << 20),), dtype=torch.uint8, device="cuda", generator=g)
+                return t[:rows * cols].view(rows, cols)
+            a, as_ = padded(m, k // 2, 0, 256), padded(m, k // 32, 118, 131)
+            b, bs = padded(n, k // 2, 0, 256), padded(n, k // 32, 118, 131)
+            A, B = fq.MXTensor(a, as_), fq.MXTensor(b, bs)
+            c0 = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            c1 = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            s = _stream(c1.device)
+
+            def vend(al):
+                return lambda i: V.fp4mx_vendor_gemm(plan, al, a.data_ptr(), as_.data_ptr(), b.data_ptr(),
+                                                     bs.data_ptr(), 1.0, c1.data_ptr(), s)
+            per_algo = []
+            for al in range(nalg.value):
+                if vend(al)(0) != 0:
+                    per_algo.append(float("inf"))
+                    continue
+                per_algo.append(_time_calls(vend(al), steps, warmup))
+                progress("  hipBLASLt algorithm %d: %.1f us" % (al, per_algo[-1] * 1e3))
+            best = int(np.argmin(per_algo))
+            tv, to = [], []
+            for _ in range(rounds):
+                to.append(_time_calls(lambda i: fq.gemm(A, B, out=c0), steps, warmup))
+                tv.append(_time_calls(vend(best), steps, warmup))
+            to, tv = float(np.median(to)), float(np.median(tv))
+            torch.cuda.synchronize()
+            diff = float(torch.linalg.vector_norm(c1 - c0) / torch.linalg.vector_norm(c0))
+            fl = 2.0 * m * n * k
+            res[key] = {"fp4mx_us": round(to * 1e3, 1), "hipblaslt_us": round(tv * 1e3, 1),
+                        "fp4mx_TFLOP/s": round(fl / (to * 1e-3) / 1e12, 1),
+                        "hipblaslt_TFLOP/s": round(fl / (tv * 1e-3) / 1e12, 1),
+                        "speedup": round(tv / to, 3), "hipblaslt_algorithms": nalg.value,
+                        "hipblaslt_per_algorithm_us": [round(x * 1e3, 1) for x in per_algo],
+                        "rel_fro_difference": diff}
+            del a, as_, b, bs, A, B, c0, c1
+        finally:
+            V.fp4mx_vendor_plan_destroy(plan)
+        torch.cuda.empty_cache()
+    return res
+
+
 def time_nvfp4_bwd(steps, warmup):
     """NVFP4 backward with MS-EDEN operands on the Quartet layer (dX and dW,
     4 MS-EDEN quantizations + 2 FP8-staged GEMMs), and the unbiased quantizers
@@ -671,12 +789,15 @@ def cpu_baseline(rows=1024, target_s=15.0):
         return time.perf_counter() - t0
 
     t_fix = run(32)
+    progress("  oracle 32 rows: %.1f s" % t_fix)
     dt = run(rows)
+    progress("  oracle %d rows: %.1f s" % (rows, dt))
     per_row = max(dt - t_fix, 1e-3) / (rows - 32)
     grown = int((target_s - t_fix) / per_row) // 32 * 32
     if grown > rows:
         rows = min(8192, grown)
         dt = run(rows)
+        progress("  oracle %d rows: %.1f s" % (rows, dt))
     flop = 6.0 * rows * n * k
     res = {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
            "sample": "linear fwd+bwd on the first %d of 8192 token rows of the 8192x4096x4096 workload "
@@ -684,6 +805,7 @@ def cpu_baseline(rows=1024, target_s=15.0):
                      "BLAS threads" % (rows, rows, dt, blas),
            "cpu_model": _cpu_model(), "host_cpus_visible": os.cpu_count()}
 
+    progress("  oracle full-size quantizer and GEMM")
     # full-size quantizer: 8192 x 4096, RHT + RTN (GEMM-0 mask)
     xq = f(synth.quantizer_tensor()["x"])
     R, Cq = xq.shape
@@ -751,8 +873,10 @@ def main():
     else:
         d = synth.llama_ffn_up(0)
         wl = {"workload": "llama3_8b_ffn_up fwd+bwd M=8192 K=4096 N=14336", "m": 8192, "n": 14336, "k": 4096}
+    progress("linear step %s" % wl["workload"])
     st, wall, avg, step_ms, dist = time_linear(d, a.steps, a.warmup,
                                               dist_steps=max(a.steps, a.dist_steps) if a.dist_steps else 0)
+    progress("linear step timed: %.4f ms" % (wall * 1e3 / a.steps))
     ev_ms = sum(avg.values())
     ms_step = wall * 1e3 / a.steps
     value = st.flops() / (ms_step * 1e-3) / 1e12
@@ -785,6 +909,7 @@ def main():
     torch.cuda.empty_cache()
     if not a.no_extra:
         if a.workload == "quartet":
+            progress("llama ffn-up step")
             st2, wall2, avg2, _, _ = time_linear(synth.llama_ffn_up(0), a.steps, a.warmup)
             ms2 = wall2 * 1e3 / a.steps
             out["llama_ffn_up"] = {"workload": "8192 x 4096 -> 14336 fwd+bwd", "ms_per_step": round(ms2, 4),
@@ -793,23 +918,35 @@ def main():
                                    "breakdown_ms": {k2: round(v, 4) for k2, v in avg2.items()}}
             del st2
             torch.cuda.empty_cache()
+        progress("gemm output dtypes")
         out["gemm_output_dtype"] = time_gemm_outputs(max(a.steps // 2, 20), 10)
         torch.cuda.empty_cache()
+        progress("quantizers")
         out["quantizer"] = time_quantizer(max(a.steps, 20), a.warmup)
         torch.cuda.empty_cache()
+        progress("nvfp4 forward")
         out["nvfp4"] = time_nvfp4(max(a.steps // 2, 5), 2)
         out["nvfp4"]["mfma_fp8_sustained"] = mfma_sustained(0)
         sus8 = out["nvfp4"]["mfma_fp8_sustained"]["random_operands"]["TFLOP/s"]
         out["nvfp4"]["frac_fp8_sustained"] = round(out["nvfp4"]["TFLOP/s"] / sus8, 4)
         torch.cuda.empty_cache()
+        progress("nvfp4 ms-eden backward")
         out["nvfp4_bwd_ms_eden"] = time_nvfp4_bwd(max(a.steps // 2, 5), 2)
         torch.cuda.empty_cache()
+        progress("quest layer")
         out["quest_linear"] = time_quest(a.steps, a.warmup)
         torch.cuda.empty_cache()
+        progress("quartet ii graph")
         out["nvfp4_quartet2"] = time_quartet2(max(a.steps // 2, 5), 2)
+    if a.vendor:
+        progress("hipBLASLt MXFP4 gemm")
+        out["vendor_gemm"] = time_vendor_gemm(20, 5)
+        torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
+        progress("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline()
-    print(json.dumps(out))
+    progress("done")
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

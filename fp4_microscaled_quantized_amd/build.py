@@ -21,6 +21,11 @@ SOURCES = ["quant_mx.hip", "gemm_mx.hip", "nvfp4.hip", "msedn.hip", "quest.hip",
 # measurement aid (the benchmark's sustained-MFMA roofline), its own library
 PROBE_SOURCES = ["probe_mfma.hip"]
 PROBE_LIB = os.path.join(PKG, "libfp4mx_probe.so")
+# measurement and cross-check aid: hipBLASLt's MXFP4 GEMM behind a C ABI (the
+# benchmark times it beside fp4mx_gemm; a GPU test compares the outputs)
+VENDOR_SOURCES = ["vendor_gemm.cpp"]
+VENDOR_LIB = os.path.join(PKG, "libfp4mx_vendor.so")
+VENDOR_LINK = ["-L/opt/rocm/lib", "-lhipblaslt"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -51,9 +56,9 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _link(objs, lib):
+def _link(objs, lib, extra=()):
     tmp = lib + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + list(extra)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
@@ -62,13 +67,15 @@ def _link(objs, lib):
 
 def build_library(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = SOURCES + PROBE_SOURCES
-    with cf.ThreadPoolExecutor(max_workers=min(7, len(srcs))) as ex:
+    srcs = SOURCES + PROBE_SOURCES + VENDOR_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], PROBE_LIB)
+    n0, n1 = len(SOURCES), len(SOURCES) + len(PROBE_SOURCES)
+    _link(objs[:n0], LIB)
+    _link(objs[n0:n1], PROBE_LIB)
+    _link(objs[n1:], VENDOR_LIB, VENDOR_LINK)
     if verbose:
-        print("built", LIB, "and", PROBE_LIB)
+        print("built", LIB, PROBE_LIB, "and", VENDOR_LIB)
     return LIB
 
 

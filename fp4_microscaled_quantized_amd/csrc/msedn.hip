@@ -150,11 +150,13 @@ __device__ __forceinline__ void msedn_core(float (&t)[32], int l4, float clip_s,
   for (int gi = 0; gi < 2; ++gi) {
     const float p = e8m3_rne(am2[gi] / clip_s);  // IEEE division
     v[gi] = p;
-    // q = E2M1_RNE(fl(y / p)): fl(y * fl(1/p)) is within 3 ulp of fl(y / p),
-    // so equal codes at v (1 -+ 2^-21) settle it (compared eight codes per
-    // word); otherwise divide exactly
-    const float rcp = p > 0.0f ? 1.0f / p : 0.0f;
-    bool exact = !(p > 0.0f) || !(rcp < __builtin_inff());
+    // q = E2M1_RNE(fl(y / p)): with r the hardware reciprocal of p (v_rcp_f32,
+    // within 1 ulp), fl(y r) is within 3 ulp of fl(y / p), so equal codes at
+    // v (1 -+ 2^-21) settle it (compared eight codes per word); otherwise, and
+    // for p outside [2^-126, 2^126], divide exactly
+    const bool normal_p = p >= 0x1p-126f && p <= 0x1p126f;
+    const float rcp = normal_p ? __builtin_amdgcn_rcpf(p) : 0.0f;
+    bool exact = !normal_p;
     uint32_t cw[2] = {0u, 0u};
     if (!exact) {
       constexpr float kLo = 1.0f - 0x1p-21f, kHi = 1.0f + 0x1p-21f;
@@ -363,12 +365,10 @@ __global__ __launch_bounds__(256) void msedn_pass1_col(
 constexpr int kNCodePitch = 68;   // code bytes per LDS row (64 + pad)
 constexpr int kNScalePitch = 12;  // scale bytes per LDS row (8 + pad)
 
-// OCP E4M3FN byte -> float (exact); 0x7F / 0xFF are NaN.
+// OCP E4M3FN byte (the low byte of b) -> float, exact, by gfx950's converter
+// v_cvt_f32_fp8 (OCP formats on this target; 0x7F / 0xFF decode to NaN).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float v = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  if ((b & 0x7Fu) == 0x7Fu) v = __builtin_nanf("");
-  return (b & 0x80u) ? -v : v;
+  return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
 }
 
 __global__ __launch_bounds__(256) void msedn_pass1_col_nv(

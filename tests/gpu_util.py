@@ -118,3 +118,29 @@ def edge_case_tensor_cols(rows: int, cols: int, seed: int = 0) -> np.ndarray:
     """edge_case_tensor with its special 32-blocks running down columns: the
     column-axis quantizer sees them as whole groups."""
     return np.ascontiguousarray(edge_case_tensor(cols, rows, seed).T)
+
+
+# ---------------------------------------------------------------------------
+# hipBLASLt's MXFP4 GEMM (libfp4mx_vendor.so, built beside libfp4mx.so).
+# ---------------------------------------------------------------------------
+_vendor = None
+
+
+def vendor_lib():
+    """ctypes handle of libfp4mx_vendor.so with its three entry points typed."""
+    import ctypes as C
+    import os
+    global _vendor
+    if _vendor is None:
+        from fp4_microscaled_quantized_amd import binding
+        path = os.path.join(os.path.dirname(binding.LIB_PATH), "libfp4mx_vendor.so")
+        L = C.CDLL(path)
+        L.fp4mx_vendor_plan_create.restype = C.c_int
+        L.fp4mx_vendor_plan_create.argtypes = [C.c_int64] * 3 + [C.POINTER(C.c_void_p), C.POINTER(C.c_int)]
+        L.fp4mx_vendor_gemm.restype = C.c_int
+        L.fp4mx_vendor_gemm.argtypes = ([C.c_void_p, C.c_int] + [C.c_void_p] * 4
+                                        + [C.c_float, C.c_void_p, C.c_void_p])
+        L.fp4mx_vendor_plan_destroy.restype = None
+        L.fp4mx_vendor_plan_destroy.argtypes = [C.c_void_p]
+        _vendor = L
+    return _vendor
