@@ -178,6 +178,33 @@ def test_nv_sr_edge_cases():
     _check_sr(synth.f32_to_bf16_bits(np.zeros((32, 32), np.float32)), 2, 1)
 
 
+@pytest.mark.parametrize("scale", [1e-38, 1e-30, 1e-12, 1.0, 1e12, 1e36])
+def test_nv_sr_scale_range(scale):
+    """Tensors across the fp32 range: the per-element quotient x / d is taken
+    by Markstein's correction only for 2^-75 <= d <= 2^100 and quotients of at
+    least 2^-25, and by exact division otherwise (tiny and huge tensors, tiny
+    elements beside normal ones); codes and scales stay bit-exact."""
+    log("nvfp4 sr scale", scale)
+    rs = np.random.default_rng(12)
+    x = (rs.standard_normal((64, 256)) * scale).astype(np.float32)
+    x[7, :5] *= np.float32(1e-9)
+    x[9, 16:32] = 0.0
+    _check_sr(synth.f32_to_bf16_bits(x), 3, 2)
+
+
+@pytest.mark.parametrize("scale", [1e-38, 1e-30, 1e12, 1e30])
+def test_msedn_scale_range(scale):
+    """MS-EDEN across the fp32 range (the pseudo-scale reciprocal is the
+    hardware one only for pseudo-scales in [2^-126, 2^126])."""
+    log("msedn scale", scale)
+    rs = np.random.default_rng(13)
+    x = (rs.standard_normal((128, 256)) * scale).astype(np.float32)
+    x[7, :5] *= np.float32(1e-9)
+    bits = synth.f32_to_bf16_bits(x)
+    _check_quant(bits, fq.ROW, 5, 1, 5)
+    _check_quant(bits, fq.COL, 5, 2, 7)
+
+
 def test_nv_sr_table1_on_gpu(golden):
     """MSE of the GPU's standard NVFP4 SR on N(0,1) matches the page's 23.5e-3."""
     want = {r[0]: float(r[1]) for r in golden("nvfp4_table1_mse.txt")}

@@ -39,6 +39,27 @@ def test_quantize46_wide_range_blocks():
     assert_bytes_equal(cpu(out.codes), c, "nv codes")
 
 
+@pytest.mark.parametrize("scale", [1e-38, 1e-30, 1e-12, 1.0, 1e12, 1e36])
+def test_quantize46_scale_range(scale):
+    """Tensors across the fp32 range.  The quotients amax_b / (c g) and
+    x / d take shortcuts (Markstein's correction, the hardware reciprocal
+    inside a bracket) only where their arguments are in range, and divide
+    exactly elsewhere; codes and scales stay bit-exact throughout."""
+    log("nv quant scale", scale)
+    rs = np.random.default_rng(11)
+    x = (rs.standard_normal((64, 256)) * scale).astype(np.float32)
+    x[7, :5] *= np.float32(1e-9)          # tiny elements beside normal ones
+    x[9, 16:32] = 0.0
+    bits = synth.f32_to_bf16_bits(x)
+    for use46 in (True, False):
+        out = fq.nv_quantize46(dev_bf16(bits), use46)
+        torch.cuda.synchronize()
+        c, s, g = nvfp4.quantize46(host_f32(bits), use46)
+        assert cpu(out.tensor_scale)[0] == g
+        assert_bytes_equal(cpu(out.scales), s, "nv scales")
+        assert_bytes_equal(cpu(out.codes), c, "nv codes")
+
+
 def test_table1_mse_from_gpu_codes(golden):
     want = {r[0]: float(r[1]) for r in golden("nvfp4_table1_mse.txt")}
     x = np.random.default_rng(0).standard_normal((1024, 1024)).astype(np.float32)
