@@ -56,6 +56,36 @@ def test_e2m1_rtn_dense_sweep_vs_textbook():
     assert np.array_equal(formats.e2m1_rtn(v), _rtn_textbook(v))
 
 
+def _rtn_textbook_vec(v):
+    """_rtn_textbook without the Python-level lookup (for large sweeps)."""
+    a = np.abs(v.astype(np.float64))
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    r = np.minimum(np.rint(a / step) * step, 6.0)
+    code = np.searchsorted(formats.E2M1_GRID, r).astype(np.uint8)
+    assert np.array_equal(formats.E2M1_GRID[code], r)
+    return code | (np.signbit(v).astype(np.uint8) << 3)
+
+
+def test_e2m1_rtn_exhaustive_over_fp32():
+    """Every fp32 input, both signs: each of the 2^23 mantissas of every
+    exponent in [2^-4, 2^4) (all grid points, midpoints and their neighbours
+    lie there), and every exponent outside that range at the mantissas where
+    a piecewise-constant rule could change (0, 1, the middle, the maximum),
+    with subnormals and zeros."""
+    mant = np.arange(1 << 23, dtype=np.uint32)
+    for e in range(123, 131):
+        for sgn in (0, 1):
+            bits = (np.uint32(sgn) << np.uint32(31)) | (np.uint32(e) << np.uint32(23)) | mant
+            v = bits.view(np.float32)
+            assert np.array_equal(formats.e2m1_rtn(v), _rtn_textbook_vec(v)), (e, sgn)
+    edge_m = np.array([0, 1, 1 << 22, (1 << 23) - 1], dtype=np.uint32)
+    ex = np.array([e for e in range(0, 255) if not 123 <= e <= 130], dtype=np.uint32)
+    bits = ((ex[:, None] << np.uint32(23)) | edge_m[None, :]).reshape(-1)
+    bits = np.concatenate([bits, bits | np.uint32(1 << 31)])
+    v = bits.view(np.float32)
+    assert np.array_equal(formats.e2m1_rtn(v), _rtn_textbook_vec(v))
+
+
 def test_e2m1_sr_exact_probability():
     # For each v, enumerate all 2^24 values of u = k 2^-24: the fraction rounding
     # up must be ceil(p 2^24) / 2^24 with p = (|v|-a)/(b-a).
@@ -141,6 +171,19 @@ def test_e8m0_code_properties():
     _, e = np.frexp(amax)
     assert np.array_equal(code, np.clip(e - 1 - 2 + 127, 0, 254))
     assert formats.e8m0_code(np.array([0.0, 6.0, 8.0, 1e-45, 3.4028235e38])).tolist() == [0, 127, 128, 0, 252]
+
+
+def test_e8m0_code_exhaustive_over_exponents():
+    """Every fp32 exponent (subnormals included) at the smallest, a middle and
+    the largest mantissa, against frexp's exponent: code = clamp(floor(log2
+    amax) - 2 + 127, 0, 254)."""
+    ex = np.arange(0, 255, dtype=np.uint32)
+    mant = np.array([1, 1 << 22, (1 << 23) - 1], dtype=np.uint32)
+    bits = ((ex[:, None] << np.uint32(23)) | mant[None, :]).reshape(-1)
+    amax = bits.view(np.float32).astype(np.float64)
+    _, e = np.frexp(amax)
+    want = np.clip(e - 1 - 2 + 127, 0, 254)
+    assert np.array_equal(formats.e8m0_code(amax).astype(np.int64), want)
 
 
 def test_e4m3_decode_matches_torch():
