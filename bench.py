@@ -944,7 +944,20 @@ def main():
         torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         progress("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline()
+        cb = cpu_baseline()
+        # GPU over oracle, the same work on each side (context only)
+        sp = {"linear_fwd_bwd_8192x4096x4096": round(value / cb["value"], 1)}
+        fs = cb["full_size"]
+        if "quantizer" in out:
+            q_s = out["quantizer"]["rtn"]["ms"] * 1e-3
+            sp["quantizer_8192x4096_rht_rtn"] = {
+                "vs_1_thread": round(fs["quantizer_8192x4096_rht_rtn"]["1_thread"]["s"] / q_s, 1),
+                "vs_all_cores": round(fs["quantizer_8192x4096_rht_rtn"]["all_cores"]["s"] / q_s, 1)}
+        g_s = out["roofline"]["mean_launch_ms"] * 1e-3
+        sp["gemm_8192x4096x4096"] = {"vs_1_thread": round(fs["gemm_8192x4096x4096"]["1_thread"]["s"] / g_s, 1),
+                                     "vs_all_cores": round(fs["gemm_8192x4096x4096"]["all_cores"]["s"] / g_s, 1)}
+        cb["gpu_speedup"] = sp
+        out["cpu_baseline"] = cb
     progress("done")
     print(json.dumps(out), flush=True)
 
