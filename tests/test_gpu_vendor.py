@@ -23,6 +23,7 @@ from gpu_util import assert_gemm_close, cpu, gemm_bound_factor, log, vendor_lib
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.timeout(600)  # hipBLASLt's first handle can take minutes to create
 @pytest.mark.parametrize("m,n,k", [(1024, 1536, 2048), (2048, 1024, 4096)])
 def test_vendor_gemm_matches(m, n, k):
     log("vendor gemm %dx%dx%d" % (m, n, k))
