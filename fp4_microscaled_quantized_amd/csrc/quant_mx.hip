@@ -46,44 +46,51 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kWaveStage = 64 * 64 + 16 * 4;  // 64 groups of 64 B, 16-B pad per 16 groups
 
-// Groups of workgroup-block `blk` (4 waves x 64 groups); `ws` is this wave's
-// LDS stage.
-template <bool HAD, int ROUND>
-__device__ __forceinline__ void row_block(uint32_t blk, uint8_t* ws, const uint16_t* __restrict__ x,
-                                          int64_t cols, int64_t ld, uint32_t sign_mask,
-                                          uint32_t key_lo, uint32_t key_hi,
-                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                          FastDiv gdiv, uint32_t ngroups) {
+// this wave's 4 x 16 B of block blk into registers (no LDS)
+__device__ __forceinline__ void row_fetch(uint32_t blk, u32x4 (&v)[4], const uint16_t* __restrict__ x,
+                                          int64_t ld, FastDiv gdiv, uint32_t ngroups) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t g_wave = blk * 256u + (uint32_t)wave * 64u;  // first group of the wave
-  if (g_wave >= ngroups) return;
-  // cooperative coalesced load: chunk q*64 + lane (16 B) of the wave's 64 groups
+  const uint32_t g_wave = blk * 256u + (uint32_t)wave * 64u;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t chunk = (uint32_t)q * 64u + (uint32_t)lane;  // 0..255
+    const uint32_t chunk = (uint32_t)q * 64u + (uint32_t)lane;
     const uint32_t g = g_wave + chunk / 4u;
     if (g < ngroups) {
       const uint32_t row32 = fastdiv(g, gdiv);
       const int64_t grp = g - row32 * gdiv.d;
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+      v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
           x + (int64_t)row32 * ld + grp * kGroup + (chunk & 3u) * 8));
-      *reinterpret_cast<u32x4*>(ws + chunk * 16 + (chunk / 64u) * 16) = v;
     }
   }
+}
+
+template <bool HAD, int ROUND>
+__device__ __forceinline__ void row_finish(uint32_t blk, const u32x4 (&v)[4], uint8_t* ws, int64_t cols,
+                                           uint32_t sign_mask, uint32_t key_lo, uint32_t key_hi,
+                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                           FastDiv gdiv, uint32_t ngroups) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t g_wave = blk * 256u + (uint32_t)wave * 64u;
+  if (g_wave >= ngroups) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t chunk = (uint32_t)q * 64u + (uint32_t)lane;
+    *reinterpret_cast<u32x4*>(ws + chunk * 16 + (chunk / 64u) * 16) = v[q];
+  }
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   const uint32_t g = g_wave + (uint32_t)lane;
-  if (g >= ngroups) return;
-  const uint32_t row32 = fastdiv(g, gdiv);
-  const int64_t row = row32, grp = g - row32 * gdiv.d;
-  const int64_t gpr = gdiv.d;
   uint32_t wd[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t chunk = (uint32_t)lane * 4u + (uint32_t)q;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ws + chunk * 16 + (chunk / 64u) * 16);
-    wd[4 * q + 0] = v.x; wd[4 * q + 1] = v.y; wd[4 * q + 2] = v.z; wd[4 * q + 3] = v.w;
+    const u32x4 w4 = *reinterpret_cast<const u32x4*>(ws + chunk * 16 + (chunk / 64u) * 16);
+    wd[4 * q + 0] = w4.x; wd[4 * q + 1] = w4.y; wd[4 * q + 2] = w4.z; wd[4 * q + 3] = w4.w;
   }
+  if (g >= ngroups) return;
+  const uint32_t row32 = fastdiv(g, gdiv);
+  const int64_t row = row32, grp = g - row32 * gdiv.d;
+  const int64_t gpr = gdiv.d;
   float t[kGroup];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -100,11 +107,19 @@ __device__ __forceinline__ void row_block(uint32_t blk, uint8_t* ws, const uint1
   scales[row * gpr + grp] = (uint8_t)sc;
 }
 
-// RTN is bandwidth-bound: a grid of about one residency (8 workgroups per CU)
-// strides over the blocks, so no partial last wave of workgroups idles the
-// memory system (8192 x 4096: 18.5 instead of 22 us).  SR runs one block per
-// workgroup: with the loop it took 6-14% longer (8192 x 4096: 30.2 against
-// 28.5 us).
+// Groups of workgroup-block `blk` (4 waves x 64 groups); `ws` is this wave's
+// LDS stage.
+template <bool HAD, int ROUND>
+__device__ __forceinline__ void row_block(uint32_t blk, uint8_t* ws, const uint16_t* __restrict__ x,
+                                          int64_t cols, int64_t ld, uint32_t sign_mask,
+                                          uint32_t key_lo, uint32_t key_hi,
+                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                          FastDiv gdiv, uint32_t ngroups) {
+  u32x4 v[4] = {};
+  row_fetch(blk, v, x, ld, gdiv, ngroups);
+  row_finish<HAD, ROUND>(blk, v, ws, cols, sign_mask, key_lo, key_hi, codes, scales, gdiv, ngroups);
+}
+
 template <bool HAD, int ROUND>
 __global__ __launch_bounds__(256) void quant_row_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint32_t sign_mask,
@@ -113,11 +128,18 @@ __global__ __launch_bounds__(256) void quant_row_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t stage[4 * kWaveStage];
   uint8_t* ws = stage + (threadIdx.x >> 6) * kWaveStage;
   if constexpr (ROUND == FP4MX_ROUND_RTN) {
-    for (uint32_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-      row_block<HAD, ROUND>(blk, ws, x, cols, ld, sign_mask, key_lo, key_hi, codes, scales, gdiv,
-                            ngroups);
+    // the next block's loads are in flight while this block is quantized
+    u32x4 cur[4] = {}, nxt[4] = {};
+    uint32_t blk = blockIdx.x;
+    if (blk < nblk) row_fetch(blk, cur, x, ld, gdiv, ngroups);
+    for (; blk < nblk; blk += gridDim.x) {
+      const uint32_t nb = blk + gridDim.x;
+      if (nb < nblk) row_fetch(nb, nxt, x, ld, gdiv, ngroups);
+      row_finish<HAD, ROUND>(blk, cur, ws, cols, sign_mask, key_lo, key_hi, codes, scales, gdiv, ngroups);
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_s_waitcnt(0xC07F);  // this block's LDS reads are done before the next writes
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
     }
   } else {
     row_block<HAD, ROUND>(blockIdx.x, ws, x, cols, ld, sign_mask, key_lo, key_hi, codes, scales,
@@ -277,7 +299,7 @@ hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64
   const FastDiv gd = make_fastdiv((uint32_t)(cols / kGroup));
   const uint32_t nblk = (uint32_t)((groups + 255) / 256);
   const uint32_t ng = (uint32_t)groups;
-  const uint32_t resident = (uint32_t)cu_count() * 8u;
+  const uint32_t resident = (uint32_t)cu_count() * 6u;
   const unsigned grid = o.rounding == FP4MX_ROUND_RTN && nblk > resident ? resident : nblk;
   if (hadamard) {
     if (o.rounding == FP4MX_ROUND_RTN)
