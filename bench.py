@@ -4,11 +4,12 @@
 One step = one pass of the whole hot path over one batch of synthetic input:
 forward (RHT + RTN quantization of X and W fused with the SR context, FP4
 GEMM Y = X W^T) and backward (RHT + SR quantization of dY and dY^T, FP4 GEMMs
-dX and dW), i.e. the kernels fp4mx_linear_fwd + fp4mx_linear_bwd launch,
-called here one by one through the C ABI.  The timed steps run back to back
-with HIP events at step boundaries only (value, ms_per_step); the same number
-of steps is then run again with an event after every launch, which gives each
-kernel's in-step duration (breakdown_ms and the roofline).
+dX and dW): fp4mx_linear_fwd + fp4mx_linear_bwd through the C ABI.  The timed
+steps run back to back with HIP events at step boundaries only (value,
+ms_per_step).  The same kernels are then launched one by one through the
+single-operation entry points with an event after every launch, which gives
+each kernel's in-step duration (breakdown_ms), and the three GEMMs back to
+back give the GEMM roofline.
 
 Headline workload: Quartet-style layer, 8192 tokens, d_in = d_out = 4096.
 value = 6*M*N*K flop / step time (TFLOP/s).  Printed as one JSON line.
@@ -78,6 +79,12 @@ class _Step:
         """Launch lists, one per input set (step i uses set i % nsets)."""
         return [self._calls(i) for i in range(getattr(self, "nsets", 1))]
 
+    def _part_calls(self):
+        """The step's kernels launched one by one, as `names` lists them (for
+        the per-launch breakdown and the GEMM pass); by default the step's
+        own launches."""
+        return self._step_calls()
+
     def run(self, steps, timed):
         """`steps` passes of the launches, back to back; when timed, one event
         before the first and one after the last launch (nothing is inserted
@@ -109,11 +116,11 @@ class _Step:
         return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
     def group_time(self, idx, steps, warmup):
-        """Mean time of one pass over the launches idx of the step (the
-        step's own calls and buffers), `steps` passes back to back between
-        one event pair after `warmup` untimed passes: ms per pass."""
+        """Mean time of one pass over the launches idx of `_part_calls` (the
+        step's kernels and buffers), `steps` passes back to back between one
+        event pair after `warmup` untimed passes: ms per pass."""
         import torch
-        sc = self._step_calls()
+        sc = self._part_calls()
         for i in range(warmup):
             for j in idx:
                 sc[i % len(sc)][j]()
@@ -127,11 +134,12 @@ class _Step:
         return ev[0].elapsed_time(ev[1]) / steps
 
     def kernel_times(self, steps):
-        """In-step duration of each launch: the same steps again with an event
-        after every launch, all on the stream the kernels run on (an event
-        record adds a few microseconds to the launch it follows)."""
+        """In-step duration of each launch: the step's kernels one by one
+        (`_part_calls`), `steps` passes with an event after every launch, all
+        on the stream the kernels run on (an event record adds a few
+        microseconds to the launch it follows)."""
         import torch
-        sc = self._step_calls()
+        sc = self._part_calls()
         evs = []
         for s_ in range(steps):
             calls = sc[s_ % len(sc)]
@@ -151,7 +159,11 @@ class _Step:
 
 
 class LinearStep(_Step):
-    """The MXFP4 linear fwd+bwd hot path as six C-ABI launches on one stream."""
+    """The MXFP4 linear fwd+bwd hot path: a step is fp4mx_linear_fwd (with the
+    backward context) + fp4mx_linear_bwd on one stream.  The same kernels
+    launched one by one through the single-operation entry points (six
+    launches: X and W quantized separately, where fp4mx_linear_fwd quantizes
+    both in one launch) give the per-launch breakdown and the GEMM pass."""
 
     def __init__(self, d, seed=0, rotate_bytes=ROTATE_BYTES):
         import torch
@@ -177,11 +189,36 @@ class LinearStep(_Step):
         self.dq, self.ds, self.dtq, self.dts = e(m, n // 2), e(m, n // 32), e(n, m // 2), e(n, m // 32)
         f = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
         self.y, self.dx, self.dw = f(m, n), f(m, k), f(n, k)
+        # the layer entry points' own outputs, context and workspace
+        self.ly, self.ldx, self.ldw = f(m, n), f(m, k), f(n, k)
+        self.lctx = fq.LinearCtx(fq.binding._alloc_mx(k, m, dev), fq.binding._alloc_mx(k, n, dev), seed)
+        self.lctx_struct = self.lctx.as_struct()
+        self.ws = fq.binding.workspace(m, n, k, dev)
         self.g = [fq.sign_mask(seed, i) for i in range(3)]
         self.names = ["quant_x", "quant_w", "gemm_y", "quant_dy", "gemm_dx", "gemm_dw"]
         self.times = {nm: [] for nm in self.names}
 
     def _calls(self, i=0):
+        """One step: fp4mx_linear_fwd with the context, then fp4mx_linear_bwd."""
+        import ctypes
+        L = self.fq.lib()
+        from fp4_microscaled_quantized_amd.binding import _check, _ptr, _stream
+        s = _stream()
+        m, n, k, seed = self.m, self.n, self.k, self.seed
+        x, w, dy = self.sets[i % self.nsets]
+        cs = ctypes.byref(self.lctx_struct)
+        return [
+            lambda: _check(L.fp4mx_linear_fwd(_ptr(x), _ptr(w), m, n, k, seed, _ptr(self.ly), cs,
+                                              _ptr(self.ws), self.ws.numel(), s)),
+            lambda: _check(L.fp4mx_linear_bwd(_ptr(dy), cs, m, n, k, _ptr(self.ldx), _ptr(self.ldw),
+                                              _ptr(self.ws), self.ws.numel(), s)),
+        ]
+
+    def _part_calls(self):
+        return [self._parts(i) for i in range(self.nsets)]
+
+    def _parts(self, i=0):
+        """The step's kernels launched one by one, in `names` order."""
         fq, L = self.fq, self.fq.lib()
         from fp4_microscaled_quantized_amd.binding import _check, _ptr, _stream
         s = _stream()
@@ -208,17 +245,18 @@ class LinearStep(_Step):
         ]
 
     def check_against_composite(self):
-        """The decomposed calls must reproduce fp4mx_linear_fwd / _bwd bit for bit."""
+        """The launches one by one must reproduce the layer entry points' step
+        bit for bit (outputs and context)."""
         import torch
-        fq = self.fq
-        self.run(1, False)
-        y, ctx = fq.linear_fwd(self.x, self.w, seed=self.seed)
-        dx, dw = fq.linear_bwd(self.dy, ctx)
+        for c in self._parts(0) + self._calls(0):
+            c()
         torch.cuda.synchronize()
-        ok = (torch.equal(y, self.y) and torch.equal(dx, self.dx) and torch.equal(dw, self.dw)
-              and torch.equal(ctx.xt.codes, self.xtq) and torch.equal(ctx.wt.scales, self.wts))
+        lc = self.lctx
+        ok = (torch.equal(self.ly, self.y) and torch.equal(self.ldx, self.dx) and torch.equal(self.ldw, self.dw)
+              and torch.equal(lc.xt.codes, self.xtq) and torch.equal(lc.xt.scales, self.xts)
+              and torch.equal(lc.wt.codes, self.wtq) and torch.equal(lc.wt.scales, self.wts))
         if not ok:
-            raise SystemExit("decomposed step differs from fp4mx_linear_fwd/bwd")
+            raise SystemExit("the launches one by one differ from fp4mx_linear_fwd/bwd")
 
 
 
@@ -892,6 +930,8 @@ def main():
         "roofline": gemm_roofline(st, avg),
         "mfma_fp4_sustained": mfma_sustained(4),
         "breakdown_ms": {k2: round(v, 4) for k2, v in avg.items()},
+        "breakdown_timing": "the step's kernels launched one by one (X and W quantized in two launches, "
+                            "which fp4mx_linear_fwd fuses into one), an event after every launch",
         "kernel_sum_ms_per_step": round(ev_ms, 4),
         "event_ms_per_step": round(float(np.mean(step_ms)), 4),
         "step_distribution": {"steps": len(dist), "median_ms": round(med, 4),

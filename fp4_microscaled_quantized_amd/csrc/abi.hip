@@ -252,8 +252,8 @@ static int linear_fwd_impl(const void* x, const void* w, int64_t m, int64_t n, i
   if (ctx) {
     QuantOut xc{FP4MX_ROUND_SR, g2, make_key(seed, 4), ctx->xt_codes, ctx->xt_scales};
     QuantOut wc{FP4MX_ROUND_SR, g1, make_key(seed, 2), ctx->wt_codes, ctx->wt_scales};
-    e = launch_quant_tile(static_cast<const uint16_t*>(x), m, k, k, true, &xr, &xc, s);
-    if (e == hipSuccess) e = launch_quant_tile(static_cast<const uint16_t*>(w), n, k, k, true, &wr, &wc, s);
+    e = launch_quant_tile_pair(static_cast<const uint16_t*>(x), m, k, k, xr, xc,
+                               static_cast<const uint16_t*>(w), n, k, k, wr, wc, s);
   } else {
     e = launch_quant_row(static_cast<const uint16_t*>(x), m, k, k, true, xr, s);
     if (e == hipSuccess) e = launch_quant_row(static_cast<const uint16_t*>(w), n, k, k, true, wr, s);

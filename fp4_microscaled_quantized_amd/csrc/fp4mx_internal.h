@@ -62,6 +62,13 @@ hipError_t launch_quant_row(const uint16_t* x, int64_t rows, int64_t cols, int64
 hipError_t launch_quant_tile(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                              bool hadamard, const QuantOut* row_out, const QuantOut* col_out,
                              hipStream_t s);
+// The dual tile quantizer (RHT) on two operands a and b, row RTN and column SR
+// for both (the linear layer's forward), in one launch; other modes, or grids
+// too large for one launch, take two.
+hipError_t launch_quant_tile_pair(const uint16_t* xa, int64_t rows_a, int64_t cols_a, int64_t ld_a,
+                                  const QuantOut& ra, const QuantOut& ca, const uint16_t* xb,
+                                  int64_t rows_b, int64_t cols_b, int64_t ld_b,
+                                  const QuantOut& rb, const QuantOut& cb, hipStream_t s);
 hipError_t launch_mx_gemm(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                           const uint8_t* bs, int64_t m, int64_t n, int64_t k, float alpha,
                           float* c, int64_t ldc, hipStream_t s);

@@ -165,15 +165,32 @@ constexpr int kTileR = 128, kTileC = 64;
 constexpr int kPitch = kTileC * 2 + 16;  // bytes per LDS row (padding vs bank conflicts)
 constexpr int kCoutPitch = (kTileR / kGroup) * 16 + 16;  // column-output staging: 64 B + pad per column
 
+// One operand of the tile kernel: its bf16 input and the row-axis and
+// column-axis outputs (the unused axis's fields are ignored).
+struct TileJob {
+  const uint16_t* x;
+  int64_t rows, cols, ld;
+  uint32_t row_mask, row_klo, row_khi;
+  uint8_t* row_codes;
+  uint8_t* row_scales;
+  uint32_t col_mask, col_klo, col_khi;
+  uint8_t* col_codes;
+  uint8_t* col_scales;
+};
+
+// The tile at rows [r0, r0 + 128) and columns [c0, c0 + 64) of job j.
 template <bool HAD, int ROW_ROUND, int COL_ROUND>
-__global__ __launch_bounds__(256) void quant_tile_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
-    uint32_t row_mask, uint32_t row_klo, uint32_t row_khi, uint8_t* __restrict__ row_codes,
-    uint8_t* __restrict__ row_scales, uint32_t col_mask, uint32_t col_klo, uint32_t col_khi,
-    uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales) {
+__device__ __forceinline__ void quant_tile(const TileJob& j, int64_t r0, int64_t c0) {
+  const uint16_t* __restrict__ x = j.x;
+  const int64_t rows = j.rows, cols = j.cols, ld = j.ld;
+  const uint32_t row_mask = j.row_mask, row_klo = j.row_klo, row_khi = j.row_khi;
+  const uint32_t col_mask = j.col_mask, col_klo = j.col_klo, col_khi = j.col_khi;
+  uint8_t* __restrict__ row_codes = j.row_codes;
+  uint8_t* __restrict__ row_scales = j.row_scales;
+  uint8_t* __restrict__ col_codes = j.col_codes;
+  uint8_t* __restrict__ col_scales = j.col_scales;
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileR * kPitch];
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * kTileR, c0 = (int64_t)blockIdx.y * kTileC;
   const int nr = (int)min<int64_t>(kTileR, rows - r0), nc = (int)min<int64_t>(kTileC, cols - c0);
 
   // Coalesced load: 1024 chunks of 16 B (8 elements), 4 per thread.
@@ -258,16 +275,40 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(
   }
 }
 
+// Grid: x = row tiles, y = column tiles.
+template <bool HAD, int RR, int CR>
+__global__ __launch_bounds__(256) void quant_tile_kernel(TileJob j) {
+  quant_tile<HAD, RR, CR>(j, (int64_t)blockIdx.x * kTileR, (int64_t)blockIdx.y * kTileC);
+}
+
+// Two operands with the same modes in one launch, so the second's tiles fill
+// the first's last partial round of workgroups: blocks [0, na) take job a's
+// tiles, the rest job b's, each in quant_tile_kernel's order (row tile
+// fastest; tra, trb = row tiles of a, b).
+template <bool HAD, int RR, int CR>
+__global__ __launch_bounds__(256) void quant_tile_pair_kernel(TileJob a, TileJob b, uint32_t na,
+                                                              uint32_t tra, uint32_t trb) {
+  const uint32_t blk = blockIdx.x;
+  const bool first = blk < na;
+  const uint32_t t = first ? blk : blk - na, tr = first ? tra : trb;
+  quant_tile<HAD, RR, CR>(first ? a : b, (int64_t)(t % tr) * kTileR, (int64_t)(t / tr) * kTileC);
+}
+
+TileJob tile_job(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const QuantOut* ro,
+                 const QuantOut* co) {
+  QuantOut z{};
+  const QuantOut& R = ro ? *ro : z;
+  const QuantOut& C = co ? *co : z;
+  return TileJob{x,       rows,     cols,     ld,          R.sign_mask, R.key.lo, R.key.hi,
+                 R.codes, R.scales, C.sign_mask, C.key.lo, C.key.hi,    C.codes,  C.scales};
+}
+
 template <bool HAD, int RR, int CR>
 hipError_t tile_launch(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                        const QuantOut* ro, const QuantOut* co, hipStream_t s) {
   dim3 grid((unsigned)((rows + kTileR - 1) / kTileR), (unsigned)((cols + kTileC - 1) / kTileC));
-  QuantOut z{};
-  const QuantOut& R = ro ? *ro : z;
-  const QuantOut& C = co ? *co : z;
-  hipLaunchKernelGGL((quant_tile_kernel<HAD, RR, CR>), grid, dim3(256), 0, s, x, rows, cols, ld,
-                     R.sign_mask, R.key.lo, R.key.hi, R.codes, R.scales, C.sign_mask, C.key.lo,
-                     C.key.hi, C.codes, C.scales);
+  hipLaunchKernelGGL((quant_tile_kernel<HAD, RR, CR>), grid, dim3(256), 0, s,
+                     tile_job(x, rows, cols, ld, ro, co));
   return hipGetLastError();
 }
 
@@ -333,6 +374,27 @@ hipError_t launch_quant_tile(const uint16_t* x, int64_t rows, int64_t cols, int6
   if (!row_out && !col_out) return hipErrorInvalidValue;
   return hadamard ? tile_dispatch<true>(x, rows, cols, ld, row_out, col_out, s)
                   : tile_dispatch<false>(x, rows, cols, ld, row_out, col_out, s);
+}
+
+hipError_t launch_quant_tile_pair(const uint16_t* xa, int64_t rows_a, int64_t cols_a, int64_t ld_a,
+                                  const QuantOut& ra, const QuantOut& ca, const uint16_t* xb,
+                                  int64_t rows_b, int64_t cols_b, int64_t ld_b,
+                                  const QuantOut& rb, const QuantOut& cb, hipStream_t s) {
+  const int64_t tra = (rows_a + kTileR - 1) / kTileR, trb = (rows_b + kTileR - 1) / kTileR;
+  const int64_t na = tra * ((cols_a + kTileC - 1) / kTileC), nb = trb * ((cols_b + kTileC - 1) / kTileC);
+  const bool fused = ra.rounding == FP4MX_ROUND_RTN && rb.rounding == FP4MX_ROUND_RTN &&
+                     ca.rounding == FP4MX_ROUND_SR && cb.rounding == FP4MX_ROUND_SR &&
+                     na + nb < (1ll << 24);  // 256 x blocks within the 32-bit grid size
+  if (!fused) {
+    hipError_t e = launch_quant_tile(xa, rows_a, cols_a, ld_a, true, &ra, &ca, s);
+    return e == hipSuccess ? launch_quant_tile(xb, rows_b, cols_b, ld_b, true, &rb, &cb, s) : e;
+  }
+  hipLaunchKernelGGL((quant_tile_pair_kernel<true, FP4MX_ROUND_RTN, FP4MX_ROUND_SR>),
+                     dim3((unsigned)(na + nb)), dim3(256), 0, s,
+                     tile_job(xa, rows_a, cols_a, ld_a, &ra, &ca),
+                     tile_job(xb, rows_b, cols_b, ld_b, &rb, &cb), (uint32_t)na, (uint32_t)tra,
+                     (uint32_t)trb);
+  return hipGetLastError();
 }
 
 }  // namespace fp4mx

@@ -157,6 +157,29 @@ def test_bf16_output_entry_points(m, n, k):
         assert_bytes_equal(bits(got), synth.f32_to_bf16_bits(cpu(want)), name + " bf16")
 
 
+@pytest.mark.parametrize("m,n,k", [(352, 96, 288), (96, 1056, 480), (1056, 2080, 1056)])
+def test_forward_one_launch_quantizer(m, n, k):
+    """fp4mx_linear_fwd quantizes X and W in one launch; its Y and context
+    equal, bit for bit, the single-operand dual quantizer on each operand
+    followed by fp4mx_gemm (shapes with ragged tiles and different tile
+    grids for X and W)."""
+    log("linear fwd one-launch quantizer", m, n, k)
+    xb = synth.normal_with_outliers((m, k), 6, 0)
+    wb = synth.normal((n, k), 0.02, 6, 1)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    seed = 23
+    y, ctx = fq.linear_fwd(x, w, seed=seed)
+    g0, g1, g2 = (fq.sign_mask(seed, i) for i in range(3))
+    xr, xc = fq.hadamard_quantize_dual(x, fq.RTN, g0, 0, fq.SR, g2, 4, seed=seed)
+    wr, wc = fq.hadamard_quantize_dual(w, fq.RTN, g0, 0, fq.SR, g1, 2, seed=seed)
+    y1 = fq.gemm(xr, wr)
+    torch.cuda.synchronize()
+    for name, a, b in (("xt", ctx.xt, xc), ("wt", ctx.wt, wc)):
+        assert_bytes_equal(cpu(a.codes), cpu(b.codes), name + " codes")
+        assert_bytes_equal(cpu(a.scales), cpu(b.scales), name + " scales")
+    assert torch.equal(y, y1)
+
+
 def test_autograd_function():
     """FP4LinearFunction under torch.autograd: Y and both gradients are the bf16
     roundings (nearest even) of fp4mx_linear_fwd / _bwd's fp32 outputs, bit for
