@@ -60,6 +60,16 @@ __device__ __forceinline__ uint32_t pair_sign(uint32_t mask, int j) {
   return (((mask >> (2 * j)) & 1u) << 15) | (((mask >> (2 * j + 1)) & 1u) << 31);
 }
 
+// Pair word w with the RHT sign flips of pair j applied, as one xor whose
+// result the unpacking then shifts and masks (the empty asm keeps the
+// compiler from splitting the xor into a half per element, which costs two
+// three-operand ops and two register copies of the constants per word).
+__device__ __forceinline__ uint32_t flip_pair(uint32_t w, uint32_t mask, int j) {
+  w ^= pair_sign(mask, j);
+  asm("" : "+v"(w));
+  return w;
+}
+
 // fmix32 of element i's counter from h1 (the group's counter after the
 // first xor-shift, see quant_group).
 __device__ __forceinline__ uint32_t sr_bits(uint32_t h1, int i) {

@@ -95,7 +95,7 @@ __device__ __forceinline__ void row_finish(uint32_t blk, const u32x4 (&v)[4], ui
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     uint32_t w = wd[j];
-    if constexpr (HAD) w ^= pair_sign(sign_mask, j);
+    if constexpr (HAD) w = flip_pair(w, sign_mask, j);
     unpack_pair(w, t[2 * j], t[2 * j + 1]);
   }
   if constexpr (HAD) fwht32(t);
@@ -219,7 +219,7 @@ __device__ __forceinline__ void quant_tile(const TileJob& j, int64_t r0, int64_t
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         uint32_t w = wd[j];
-        if constexpr (HAD) w ^= pair_sign(row_mask, j);
+        if constexpr (HAD) w = flip_pair(w, row_mask, j);
         unpack_pair(w, t[2 * j], t[2 * j + 1]);
       }
       if constexpr (HAD) fwht32(t);

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void quest_row_kernel(
   }
   float t[kGroup];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) unpack_pair(wd[j] ^ pair_sign(sign_mask, j), t[2 * j], t[2 * j + 1]);
+  for (int j = 0; j < 16; ++j) unpack_pair(flip_pair(wd[j], sign_mask, j), t[2 * j], t[2 * j + 1]);
   fwht32(t);
   uint32_t w[4], sc, mb;
   quest_group(t, clip, w, sc, mb);
