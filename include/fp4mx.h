@@ -13,7 +13,9 @@
  *   stream has been synchronised.  No state carries from one call to the
  *   next except per-device caches of two device queries (the architecture
  *   check and the compute-unit count), each written once per device and safe
- *   to read from any thread.
+ *   to read from any thread, and the static device scratch array that
+ *   fp4nv_msedn_quantize_noalloc works in (it keeps the last call's
+ *   contents; that entry point's comment has the rules).
  * - Device check: a current device other than gfx950 gives FP4MX_E_DEVICE.
  *   The environment variable FP4MX_DEVICE_ARCH, when set to another
  *   architecture name, makes every compute call return FP4MX_E_DEVICE after
