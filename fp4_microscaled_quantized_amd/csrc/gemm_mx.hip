@@ -284,7 +284,14 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[kBM / WM / 32][kBN /
   }
 }
 
-template <int FMT, bool VEC, int WM, int WN, int EPI>
+// Scale-row load modes (SCL): 0 one byte per group (K not a multiple of the
+// stage), 1 one 8-B (FP4) or 4-B (FP8) load per row per stage, 2 (FP4 only)
+// one 16-B load per row every second stage (K/32 a multiple of 16, scale
+// pointers 16-B aligned).  A row's scale bytes for one stage lie in their
+// own cache line, so each scale load instruction touches 64 lines; mode 2
+// halves the scale load instructions and the lines they touch (measured
+// 0.5-2.5% faster on the linear-layer shapes, bit-identical output).
+template <int FMT, int SCL, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, int M, int N, int K, float alpha,
@@ -318,7 +325,9 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
   // Scale bytes go through registers and are rearranged after the MFMAs.
   constexpr int kSR = (kBM + kBN) / kThreads;  // scale rows per thread (2 or 1)
   uint32_t rsw[kSR][2];  // raw scale words of this thread's scale rows (8 groups)
+  uint32_t rsq[kSR][4] = {};  // SCL 2: 16 B of scale bytes = two stages
   uint32_t rsb[kSR][8];  // byte-wise scale loads (K not a stage multiple)
+  static_assert(SCL != 2 || F::kGroups == 8, "scale mode 2 is FP4 only");
   // Per-lane part of the load offsets: row 8b + l/8 of block b and the
   // swizzled chunk, which depends only on the parity of b (rows 8b..8b+7
   // have (row >> 1) & 7 = 4 (b & 1) + (l/8)/2).  The block part b*8*kbytes is
@@ -359,7 +368,14 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
       const rsrc_t rr = isA ? rAs : rBs;
       const uint32_t base_s =
           (((uint32_t)(kSR == 2 ? tid : tid & 255) * kgroups + g0) & ~all_off) | (kOOB & all_off);
-      if constexpr (VEC) {
+      if constexpr (SCL == 2) {
+        // wave-uniform: each even stage fetches its own and the next stage's
+        if ((st & 1) == 0) {
+          const i32x4 v = buf_load16(rr, base_s);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rsq[w][q] = (uint32_t)v[q];
+        }
+      } else if constexpr (SCL == 1) {
         if constexpr (F::kGroups == 8) {
           const i32x2 v = buf_load8(rr, base_s);
           rsw[w][0] = (uint32_t)v.x;
@@ -378,15 +394,24 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
       }
     }
   };
-  auto sstore = [&](int buf) {
+  // st: the stage whose scales are stored
+  auto sstore = [&](int buf, int st) {
     uint8_t* base = lds + buf * kStageLds;
+    if constexpr (SCL == 2) {
+      const bool odd = st & 1;  // wave-uniform
+#pragma unroll
+      for (int w = 0; w < kSR; ++w) {
+        rsw[w][0] = odd ? rsq[w][2] : rsq[w][0];
+        rsw[w][1] = odd ? rsq[w][3] : rsq[w][1];
+      }
+    }
     // dword h of a row holds groups h, 2+h, 4+h, 6+h: in K-substep s the
     // lanes of half h carry group 2s+h's scale (byte s, picked by op_sel)
     uint32_t* sp = reinterpret_cast<uint32_t*>(base + kCodeLds);
 #pragma unroll
     for (int w = 0; w < kSR; ++w) {
       uint32_t b[8];
-      if constexpr (VEC) {
+      if constexpr (SCL >= 1) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           b[j] = (rsw[w][0] >> (8 * j)) & 0xFFu;
@@ -430,7 +455,7 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
 
   gload_codes(0, 0, 0, 1, true);
   gload_scales(0, true);
-  sstore(0);
+  sstore(0, 0);
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): stage 0 is in LDS
   __syncthreads();
 
@@ -504,7 +529,7 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
       sub(std::integral_constant<int, 2>{});
       sub(std::integral_constant<int, 3>{});
     }
-    sstore((st + 1) & 1);
+    sstore((st + 1) & 1, st + 1);
     // keep this stage's MFMAs above the wait: otherwise the scheduler sinks
     // them below it and the next stage's loads stop overlapping the math
     __builtin_amdgcn_sched_barrier(0);
@@ -515,17 +540,17 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
   gemm_epilogue<EPI, WM, WN>(acc, lds, lane, wave, m0, n0, M, N, ldc, alpha, C, cmask, sign_mask);
 }
 
-template <int FMT, bool VEC, int WM, int WN, int EPI>
+template <int FMT, int SCL, int WM, int WN, int EPI>
 hipError_t gemm_launch_cfg(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                            int64_t m, int64_t n, int64_t k, float alpha, const float* ga,
                            const float* gb, float* c, int64_t ldc, const uint32_t* cmask,
                            uint32_t sign_mask, hipStream_t s) {
   const size_t lds = 2 * (size_t)kStageLds;
-  const void* fn = reinterpret_cast<const void*>(&mx_gemm_kernel<FMT, VEC, WM, WN, EPI>);
+  const void* fn = reinterpret_cast<const void*>(&mx_gemm_kernel<FMT, SCL, WM, WN, EPI>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
-  hipLaunchKernelGGL((mx_gemm_kernel<FMT, VEC, WM, WN, EPI>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((mx_gemm_kernel<FMT, SCL, WM, WN, EPI>), dim3((unsigned)tiles),
                      dim3(Waves<WM, WN>::kThreads), lds, s, a, as, b, bs, (int)m, (int)n, (int)k,
                      alpha, ga, gb, c, (int)ldc, cmask, sign_mask);
   return hipGetLastError();
@@ -536,12 +561,19 @@ hipError_t gemm_launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, co
                        int64_t m, int64_t n, int64_t k, float alpha, const float* ga,
                        const float* gb, float* c, int64_t ldc, const uint32_t* cmask,
                        uint32_t sign_mask, hipStream_t s) {
-  // scale rows split into whole per-stage words when K is a stage multiple
-  const bool vec = (k / 32) % Fmt<FMT>::kGroups == 0;
-  if (vec)
-    return gemm_launch_cfg<FMT, true, FP4MX_GEMM_WM, FP4MX_GEMM_WN, EPI>(
+  // scale rows split into whole per-stage words when K is a stage multiple,
+  // and into whole 16-B packs when K/32 is a multiple of 16
+  const int64_t kg = k / 32;
+  const bool a16 = (((uintptr_t)as | (uintptr_t)bs) & 15u) == 0;
+  if constexpr (FMT == 4) {
+    if (kg % 16 == 0 && a16)
+      return gemm_launch_cfg<FMT, 2, FP4MX_GEMM_WM, FP4MX_GEMM_WN, EPI>(
+          a, as, b, bs, m, n, k, alpha, ga, gb, c, ldc, cmask, sign_mask, s);
+  }
+  if (kg % Fmt<FMT>::kGroups == 0)
+    return gemm_launch_cfg<FMT, 1, FP4MX_GEMM_WM, FP4MX_GEMM_WN, EPI>(
         a, as, b, bs, m, n, k, alpha, ga, gb, c, ldc, cmask, sign_mask, s);
-  return gemm_launch_cfg<FMT, false, FP4MX_GEMM_WM, FP4MX_GEMM_WN, EPI>(
+  return gemm_launch_cfg<FMT, 0, FP4MX_GEMM_WM, FP4MX_GEMM_WN, EPI>(
       a, as, b, bs, m, n, k, alpha, ga, gb, c, ldc, cmask, sign_mask, s);
 }
 

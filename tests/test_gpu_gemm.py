@@ -56,6 +56,32 @@ def test_gemm_parity_xcd_remap(m, n, k):
     assert_gemm_close(c, mx.dequantize(*qa), mx.dequantize(*qb), mx.ALPHA_BWD, "remap %dx%dx%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("m,n,k,off", [(256, 512, 1024, 1), (288, 544, 4096, 8), (512, 256, 2560, 4)])
+def test_gemm_scale_pointer_alignment(m, n, k, off):
+    """Scale pointers off 16-B alignment (byte offsets 1, 8, 4) take the
+    per-stage scale loads; aligned ones with K/32 a multiple of 16 take the
+    16-B loads every second stage.  Both are bit-identical and match the
+    oracle's product element-wise."""
+    log("gemm scale alignment", m, n, k, off)
+    a, b = _operands(m, n, k, seed=4)
+    qa = mx.quantize(host_f32(a), rounding=mx.SR, sign_mask=5, seed=2, stream=3)
+    qb = mx.quantize(host_f32(b), rounding=mx.RTN, sign_mask=5)
+
+    def shifted(scales):
+        buf = torch.zeros(scales.size + 32, dtype=torch.uint8, device="cuda")
+        t = buf[off:off + scales.size].view(scales.shape)
+        t.copy_(torch.from_numpy(scales))
+        assert t.data_ptr() % 16 == off % 16
+        return t
+
+    c0 = fq.gemm(_to_dev_mx(*qa), _to_dev_mx(*qb), alpha=1.25)
+    c1 = fq.gemm(fq.MXTensor(torch.from_numpy(qa[0]).cuda(), shifted(qa[1])),
+                 fq.MXTensor(torch.from_numpy(qb[0]).cuda(), shifted(qb[1])), alpha=1.25)
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1)
+    assert_gemm_close(cpu(c1), mx.dequantize(*qa), mx.dequantize(*qb), 1.25, "scale alignment")
+
+
 def test_gemm_output_stride_and_alpha():
     a, b = _operands(64, 96, 256)
     qa = mx.quantize(host_f32(a), rounding=mx.RTN)
