@@ -285,12 +285,12 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[kBM / WM / 32][kBN /
 }
 
 // Scale-row load modes (SCL): 0 one byte per group (K not a multiple of the
-// stage), 1 one 8-B (FP4) or 4-B (FP8) load per row per stage, 2 (FP4 only)
-// one 16-B load per row every second stage (K/32 a multiple of 16, scale
-// pointers 16-B aligned).  A row's scale bytes for one stage lie in their
-// own cache line, so each scale load instruction touches 64 lines; mode 2
-// halves the scale load instructions and the lines they touch (measured
-// 0.5-2.5% faster on the linear-layer shapes, bit-identical output).
+// stage), 1 one 8-B (FP4) or 4-B (FP8) load per row per stage, 2 one 16-B
+// load per row every kPack stages (FP4: 2, FP8: 4; K/32 a multiple of 16,
+// scale pointers 16-B aligned).  A row's scale bytes for one stage lie in
+// their own cache line, so each scale load instruction touches 64 lines;
+// mode 2 issues 1/2 (FP4) or 1/4 (FP8) as many (measured 0.5-2.5% faster on
+// the FP4 linear-layer shapes, bit-identical output).
 template <int FMT, int SCL, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
@@ -325,9 +325,9 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
   // Scale bytes go through registers and are rearranged after the MFMAs.
   constexpr int kSR = (kBM + kBN) / kThreads;  // scale rows per thread (2 or 1)
   uint32_t rsw[kSR][2];  // raw scale words of this thread's scale rows (8 groups)
-  uint32_t rsq[kSR][4] = {};  // SCL 2: 16 B of scale bytes = two stages
+  uint32_t rsq[kSR][4] = {};  // SCL 2: 16 B of scale bytes = kPack stages
   uint32_t rsb[kSR][8];  // byte-wise scale loads (K not a stage multiple)
-  static_assert(SCL != 2 || F::kGroups == 8, "scale mode 2 is FP4 only");
+  constexpr int kPack = 16 / F::kGroups;
   // Per-lane part of the load offsets: row 8b + l/8 of block b and the
   // swizzled chunk, which depends only on the parity of b (rows 8b..8b+7
   // have (row >> 1) & 7 = 4 (b & 1) + (l/8)/2).  The block part b*8*kbytes is
@@ -369,8 +369,8 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
       const uint32_t base_s =
           (((uint32_t)(kSR == 2 ? tid : tid & 255) * kgroups + g0) & ~all_off) | (kOOB & all_off);
       if constexpr (SCL == 2) {
-        // wave-uniform: each even stage fetches its own and the next stage's
-        if ((st & 1) == 0) {
+        // wave-uniform: the first stage of each pack fetches the whole pack
+        if (st % kPack == 0) {
           const i32x4 v = buf_load16(rr, base_s);
 #pragma unroll
           for (int q = 0; q < 4; ++q) rsq[w][q] = (uint32_t)v[q];
@@ -401,8 +401,15 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
       const bool odd = st & 1;  // wave-uniform
 #pragma unroll
       for (int w = 0; w < kSR; ++w) {
-        rsw[w][0] = odd ? rsq[w][2] : rsq[w][0];
-        rsw[w][1] = odd ? rsq[w][3] : rsq[w][1];
+        if constexpr (kPack == 2) {
+          rsw[w][0] = odd ? rsq[w][2] : rsq[w][0];
+          rsw[w][1] = odd ? rsq[w][3] : rsq[w][1];
+        } else {
+          const uint32_t s01 = odd ? rsq[w][1] : rsq[w][0];
+          const uint32_t s23 = odd ? rsq[w][3] : rsq[w][2];
+          rsw[w][0] = (st & 2) ? s23 : s01;
+          rsw[w][1] = 0;
+        }
       }
     }
     // dword h of a row holds groups h, 2+h, 4+h, 6+h: in K-substep s the
@@ -565,11 +572,9 @@ hipError_t gemm_launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, co
   // and into whole 16-B packs when K/32 is a multiple of 16
   const int64_t kg = k / 32;
   const bool a16 = (((uintptr_t)as | (uintptr_t)bs) & 15u) == 0;
-  if constexpr (FMT == 4) {
-    if (kg % 16 == 0 && a16)
-      return gemm_launch_cfg<FMT, 2, FP4MX_GEMM_WM, FP4MX_GEMM_WN, EPI>(
-          a, as, b, bs, m, n, k, alpha, ga, gb, c, ldc, cmask, sign_mask, s);
-  }
+  if (kg % 16 == 0 && a16)
+    return gemm_launch_cfg<FMT, 2, FP4MX_GEMM_WM, FP4MX_GEMM_WN, EPI>(
+        a, as, b, bs, m, n, k, alpha, ga, gb, c, ldc, cmask, sign_mask, s);
   if (kg % Fmt<FMT>::kGroups == 0)
     return gemm_launch_cfg<FMT, 1, FP4MX_GEMM_WM, FP4MX_GEMM_WN, EPI>(
         a, as, b, bs, m, n, k, alpha, ga, gb, c, ldc, cmask, sign_mask, s);
