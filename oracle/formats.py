@@ -75,29 +75,6 @@ def _e2m1_rtn_flat(v: np.ndarray) -> np.ndarray:
     return code.reshape(v.shape) | _sign_bit(v)
 
 
-def e2m1_sr(v: np.ndarray, u: np.ndarray) -> np.ndarray:
-    """Stochastic rounding onto the E2M1 grid with uniform draws ``u`` in [0,1).
-
-    For a <= |v| < b with a, b adjacent grid points, the magnitude is b with
-    probability (|v|-a)/(b-a) and a otherwise ("NVFP4 Format and Standard
-    Stochastic Rounding", Step 3): here b is taken iff u < (|v|-a)/(b-a).
-    Requires |v| <= 6 (the callers' scales guarantee no clipping).
-    """
-    v = np.asarray(v, dtype=np.float32)
-    a = np.abs(v.astype(np.float64))
-    if np.any(a > 6.0):
-        raise ValueError("e2m1_sr needs |v| <= 6")
-    lo = np.searchsorted(E2M1_GRID, a, side="right") - 1          # grid[lo] <= a
-    lo = np.minimum(lo, 7)
-    hi = np.minimum(lo + 1, 7)
-    ga, gb = E2M1_GRID[lo], E2M1_GRID[hi]
-    gap = np.where(hi > lo, gb - ga, 1.0)
-    p = np.where(hi > lo, (a - ga) / gap, 0.0)
-    up = np.asarray(u, dtype=np.float64) < p
-    code = np.where(up, hi, lo).astype(np.uint8)
-    return code | _sign_bit(v)
-
-
 def e2m1_sr_carry(v: np.ndarray, r: np.ndarray) -> np.ndarray:
     """Stochastic rounding onto the E2M1 grid driven by 32 random bits ``r``
     per element: the MXFP4 quantizer's backward rounding.

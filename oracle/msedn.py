@@ -245,6 +245,15 @@ GUARD_D = np.float32(GUARD_C * np.float32(448.0))
 def sr_quantize(x: np.ndarray, seed: int, stream: int):
     """Q_SR of x [R, C] (groups of 16 along rows).
 
+    Tensor scale with the 16/17 guard, E4M3 group scales by RNE, then each
+    v = fl(x / fl(s16 g)), clamped to [-6, 6], rounded stochastically onto
+    the E2M1 grid ("Quartet II ...", "NVFP4 Format and Standard Stochastic
+    Rounding").  The pages fix the rounding probability p = (|v|-a)/(b-a);
+    the random bits realise it by the same 22-bit carry rule as the MXFP4
+    backward quantizer (``formats.e2m1_sr_carry`` on the counter hash at
+    index row * C + col): unbiased for every |v| >= 1, short of p by less
+    than 2^-22 below 1.
+
     Returns (codes [R, C/2] uint8, scales [R, C/16] E4M3 uint8, g float32)."""
     a = np.asarray(x, dtype=np.float32)
     R, C = a.shape
@@ -263,6 +272,5 @@ def sr_quantize(x: np.ndarray, seed: int, stream: int):
     v = np.clip(v, np.float32(-6.0), np.float32(6.0)).reshape(R, C)
     idx = (np.arange(R, dtype=np.uint64)[:, None] * np.uint64(C)
            + np.arange(C, dtype=np.uint64)[None, :])
-    u = rng.uniform24(rng.bits(seed, stream, idx))
-    q = formats.e2m1_sr(v, u)
+    q = formats.e2m1_sr_carry(v, rng.bits(seed, stream, idx))
     return _pack(q), s_code, g

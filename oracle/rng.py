@@ -17,8 +17,9 @@ from two published mixing functions,
 Per (seed, stream): key = splitmix64(seed XOR (stream << 32)).
 Per element with output-operand linear index i = row * cols + col:
     r(i) = fmix32(lo32(i) ^ lo32(key) ^ fmix32(hi32(i) ^ hi32(key))).
-The MXFP4 quantizer's SR draw is u = (r >> 10) * 2^-22 (formats.e2m1_sr_carry);
-the NVFP4 SR baseline and MS-EDEN draw u = (r >> 8) * 2^-24.
+The E2M1 stochastic roundings (the MXFP4 quantizers and the NVFP4 SR
+baseline) draw u = (r >> 10) * 2^-22 (formats.e2m1_sr_carry); MS-EDEN's E4M3
+scale rounding draws u = (r >> 8) * 2^-24.
 RHT sign mask of GEMM g: lo32(splitmix64(seed XOR ((0x5100 + g) << 32))).
 """
 from __future__ import annotations
