@@ -37,6 +37,9 @@ METRIC = "MXFP4 linear fwd+bwd TFLOPS (% FP4 MFMA peak); quantizer GB/s (% HBM)"
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# vector ALU issue: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz, one 64-lane wave
+# instruction per SIMD every 4 cycles (a transcendental takes 12 more)
+PEAK_VALU_TLANE = 256 * 4 * 16 * 2.4e9 / 1e12
 MX_BYTES_PER_ELEM = 2 + 0.5 + 1 / 32   # bf16 in, 4-bit code + 1/32 scale byte out
 ROTATE_BYTES = 1 << 30                  # linear-layer inputs in rotation: at least 1 GiB
 DIST_STEPS = 200                        # steps timed one by one for the median
@@ -472,6 +475,37 @@ def quant_roofline(st, avg):
     gbs = sum(by.values()) / (sum(avg[x] for x in by) * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+QUANT_VALU_RECORD = os.path.join(ROOT, "profiles", "quantizer_in_step_valu_record.json")
+
+
+def quant_alu_roofline(st, avg):
+    """ALU roofline of the step's three quantizer launches: the VALU
+    instructions each issues (committed SQ_INSTS_VALU / SQ_INSTS_VALU_TRANS_F32
+    record, taken on this exact quantizer source and workload) against the
+    chip's vector issue rate; None when the record does not match."""
+    import hashlib
+    try:
+        with open(QUANT_VALU_RECORD) as f:
+            rec = json.load(f)
+        for src, sha in rec["source_sha256"].items():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != sha:
+                    return None
+    except (OSError, ValueError, KeyError):
+        return None
+    if "%dx%dx%d" % (st.m, st.n, st.k) != rec["workload"]:
+        return None
+    keys = ("quant_x", "quant_w", "quant_dy")
+    lane_instr = sum(64.0 * (rec["valu_per_launch"][x] + 3.0 * rec["trans_per_launch"][x]) for x in keys)
+    t = sum(avg[x] for x in keys) * 1e-3
+    ach = lane_instr / t / 1e12
+    return {"bound": "alu", "achieved": round(ach, 2), "peak": round(PEAK_VALU_TLANE, 2),
+            "unit": "T VALU lane-instructions/s (a transcendental counts 4)",
+            "frac": round(ach / PEAK_VALU_TLANE, 4),
+            "valu_per_launch": {x: rec["valu_per_launch"][x] for x in keys},
+            "record": os.path.relpath(QUANT_VALU_RECORD, ROOT)}
 
 
 def time_quantizer(steps, warmup, nbuf=6):
@@ -941,6 +975,7 @@ def main():
                               "median_TFLOP/s": round(st.flops() / (med * 1e-3) / 1e12, 1),
                               "note": "one event at every step boundary, inputs rotating over the sets above"},
         "quantizer_roofline_in_step": quant_roofline(st, avg),
+        "quantizer_alu_roofline_in_step": quant_alu_roofline(st, avg),
     }
     sus = out["mfma_fp4_sustained"]["random_operands"]["TFLOP/s"]
     out["roofline"]["sustained_peak_random_operands"] = sus
