@@ -1,5 +1,6 @@
 // Per-group device arithmetic shared by the MXFP4 kernels (quant_mx.hip,
-// quest.hip): the in-register block-32 FWHT, bf16 unpacking and sign flips,
+// quest.hip; nvfp4.hip's SR baseline takes the hash and the SR converter
+// helpers): the in-register block-32 FWHT, bf16 unpacking and sign flips,
 // the counter hash of the SR draws, and the MX group quantizer (E8M0 scale
 // from the group maximum; RTN and SR by the hardware converters, SR taking
 // the top 22 bits of each element's draw).
