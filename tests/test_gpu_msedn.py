@@ -176,6 +176,17 @@ def test_nv_sr_edge_cases():
     x[5] = 1e-38
     _check_sr(synth.f32_to_bf16_bits(x), 2, 1)
     _check_sr(synth.f32_to_bf16_bits(np.zeros((32, 32), np.float32)), 2, 1)
+    # groups with normal scales holding: -0 beside nonzero values (the
+    # quotient keeps x's sign); bf16 subnormals and tiny quotients (below
+    # 2^-23, rounded to a signed zero) beside normal values; one repeated
+    # value (every element at the group maximum)
+    y = rs.standard_normal((32, 64)).astype(np.float32)
+    y[6, :16] = np.where(np.arange(16) % 2 == 0, -0.0, rs.standard_normal(16))
+    y[8, 16:32] = np.concatenate([[1.0, -2.0, 1e-39, -1e-39, 5e-40, -5e-40],
+                                  np.ldexp(rs.choice([-1.0, 1.0], 10), -rs.integers(20, 60, 10))])
+    y[10, :16] = 3.25
+    y[10, 16:32] = -3.25
+    _check_sr(synth.f32_to_bf16_bits(y), 5, 3)
 
 
 @pytest.mark.parametrize("scale", [1e-38, 1e-30, 1e-12, 1.0, 1e12, 1e36])
