@@ -39,6 +39,26 @@ def test_quantize46_wide_range_blocks():
     assert_bytes_equal(cpu(out.codes), c, "nv codes")
 
 
+def test_quantize46_signed_zeros_and_subnormals():
+    """Groups with normal scales holding -0 beside nonzero values (the code
+    keeps x's sign bit), bf16 subnormals and tiny values beside normal ones,
+    and one repeated value."""
+    rs = np.random.default_rng(8)
+    x = rs.standard_normal((32, 64)).astype(np.float32)
+    x[2, :16] = np.where(np.arange(16) % 2 == 0, -0.0, rs.standard_normal(16))
+    x[3, 16:32] = np.where(np.arange(16) % 3 == 0, 0.0, -rs.random(16))
+    x[4, :16] = np.concatenate([[1.0, -2.0, 1e-39, -1e-39, 5e-40, -5e-40],
+                                np.ldexp(rs.choice([-1.0, 1.0], 10), -rs.integers(20, 60, 10))])
+    x[5, :16] = -2.5
+    bits = synth.f32_to_bf16_bits(x)
+    for use46 in (True, False):
+        out = fq.nv_quantize46(dev_bf16(bits), use46)
+        torch.cuda.synchronize()
+        c, s, g = nvfp4.quantize46(host_f32(bits), use46)
+        assert_bytes_equal(cpu(out.scales), s, "nv scales")
+        assert_bytes_equal(cpu(out.codes), c, "nv codes")
+
+
 @pytest.mark.parametrize("scale", [1e-38, 1e-30, 1e-12, 1.0, 1e12, 1e36])
 def test_quantize46_scale_range(scale):
     """Tensors across the fp32 range.  The quotients amax_b / (c g) and
