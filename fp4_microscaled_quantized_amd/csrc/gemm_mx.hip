@@ -196,6 +196,23 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[kBM / WM / 32][kBN /
     const int gpr = N / 32;  // mask words per row
     const rsrc_t rM = make_rsrc(EPI == kEpiIrht ? cmask + (size_t)m0 * gpr : nullptr,
                                 EPI == kEpiIrht ? (uint32_t)rowsC * (uint32_t)gpr * 4u : 0u);
+    // IRHT: the lane's mask words of all FM blocks are loaded up front, so
+    // their latency overlaps the staging of the first block
+    uint32_t mbw[FM][2] = {};
+    if constexpr (EPI == kEpiIrht) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int item = lane + 64 * u;             // 32 rows x 4 groups
+          const int rl = item >> 2, gq = item & 3;
+          const int col0 = n0 + wn * (kBN / WN) + 32 * gq;
+          const uint32_t badc = 0u - (uint32_t)(col0 >= N);
+          const int row = wm * (kBM / WM) + i * 32 + rl;
+          const uint32_t moff = ((((uint32_t)row * (uint32_t)gpr + (uint32_t)(col0 >> 5)) * 4u) & ~badc) | (kOOB & badc);
+          mbw[i][u] = buf_load4(rM, moff);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -216,11 +233,7 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[kBM / WM / 32][kBN /
             const float4 w = *reinterpret_cast<const float4*>(stg + rl * 132 + 32 * gq + 4 * q);
             t[4 * q] = w.x; t[4 * q + 1] = w.y; t[4 * q + 2] = w.z; t[4 * q + 3] = w.w;
           }
-          const int col0 = n0 + wn * (kBN / WN) + 32 * gq;     // first column of the group
-          const uint32_t badc = 0u - (uint32_t)(col0 >= N);
-          const int row = wm * (kBM / WM) + i * 32 + rl;       // within the tile
-          const uint32_t moff = ((((uint32_t)row * (uint32_t)gpr + (uint32_t)(col0 >> 5)) * 4u) & ~badc) | (kOOB & badc);
-          const uint32_t mb = buf_load4(rM, moff);
+          const uint32_t mb = mbw[i][u];
 #pragma unroll
           for (int e = 0; e < 32; ++e) t[e] = ((mb >> e) & 1u) ? 0.0f : t[e];
 #pragma unroll
