@@ -302,8 +302,9 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[kBM / WM / 32][kBN /
 // load per row every kPack stages (FP4: 2, FP8: 4; K/32 a multiple of 16,
 // scale pointers 16-B aligned).  A row's scale bytes for one stage lie in
 // their own cache line, so each scale load instruction touches 64 lines;
-// mode 2 issues 1/2 (FP4) or 1/4 (FP8) as many (measured 0.5-2.5% faster on
-// the FP4 linear-layer shapes, bit-identical output).
+// mode 2 issues 1/2 (FP4) or 1/4 (FP8) as many (measured bit-identical and
+// 0.5-2.5% faster on the FP4 linear-layer shapes, 4-6% on the staged FP8
+// GEMM).
 template <int FMT, int SCL, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64, WM * WN / 4) void mx_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
