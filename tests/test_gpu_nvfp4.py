@@ -13,6 +13,25 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
 
+@pytest.mark.parametrize("shape", [(32, 96), (1056, 4128), (4160, 8192)])
+def test_tensor_scale_max_position(shape):
+    """g = fl32(max|x| / 1536) with the largest magnitude planted first, last
+    and in the middle of the tensor, negative or positive.  The chunk counts
+    (16 B each) are not multiples of a workgroup's 2048, and the largest shape
+    (4.26 M chunks) takes two passes of the flat reduction's grid."""
+    r, c = shape
+    base = synth.normal(shape, 1.0, 11, 0)
+    for pos, val in ((0, -50.0), (r * c - 1, 60.0), (r * c // 2 + 7, -70.0)):
+        bits = base.copy().reshape(-1)
+        bits[pos] = synth.f32_to_bf16_bits(np.array([val], dtype=np.float32))[0]
+        bits = bits.reshape(shape)
+        log("tensor scale", shape, "max at", pos)
+        out = fq.nv_quantize46(dev_bf16(bits), True)
+        torch.cuda.synchronize()
+        g = nvfp4.tensor_scale(host_f32(bits))
+        assert cpu(out.tensor_scale)[0] == g
+
+
 @pytest.mark.parametrize("shape", [(64, 128), (96, 160), (32, 32), (512, 1024)])
 @pytest.mark.parametrize("use46", [True, False])
 def test_quantize46_bit_exact(shape, use46):
